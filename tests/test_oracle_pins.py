@@ -1,0 +1,349 @@
+"""Pins for the CPU oracle: it is checked against things other than itself.
+
+Each test states which property of the definition it pins.  Nothing here
+needs a GPU.  See oracle/attention.py for the definition being pinned.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as wl
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def rnd(shape, seed):
+    return np.random.default_rng(seed).standard_normal(shape)
+
+
+# ----------------------------------------------------------------------------
+# widening of storage bits (pinned to fixed bit patterns and to torch's casts)
+# ----------------------------------------------------------------------------
+def test_widen_fixed_bit_patterns():
+    bf = np.array([0x3F80, 0xC000, 0x0000, 0x8000, 0x7F80, 0xFF80, 0x0001, 0x3FC0, 0x4049],
+                  dtype=np.uint16)
+    got = oracle.widen(bf, "bf16")
+    want = [1.0, -2.0, 0.0, -0.0, math.inf, -math.inf, 2.0 ** -133, 1.5, 3.140625]
+    assert got.tolist() == want
+    assert math.copysign(1.0, got[3]) == -1.0
+    fp = np.array([0x3C00, 0xC000, 0x0001, 0x7BFF, 0x3555], dtype=np.uint16)
+    got = oracle.widen(fp, "fp16")
+    assert got.tolist() == [1.0, -2.0, 2.0 ** -24, 65504.0, 0.333251953125]
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp16"])
+def test_generator_rounding_matches_torch_cast(dtype):
+    x = np.random.default_rng(7).standard_normal(50000).astype(np.float32) * 3
+    x[:4] = [1.00390625, 1.01171875, -1.00390625, 65519.0]  # ties and near-overflow
+    bits = wl.to_bits(x, dtype)
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float16
+    want = torch.from_numpy(x).to(tdt).to(torch.float64).numpy()
+    np.testing.assert_array_equal(oracle.widen(bits, dtype), want)
+
+
+# ----------------------------------------------------------------------------
+# brute force on tiny shapes: pure-Python loops with math.exp
+# ----------------------------------------------------------------------------
+def brute(q, k, v, causal, scale):
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    g = Hq // Hkv
+    o = np.zeros((B, Hq, Sq, v.shape[3]))
+    for b in range(B):
+        for h in range(Hq):
+            for i in range(Sq):
+                keys = [j for j in range(Sk) if (not causal) or j <= i + Sk - Sq]
+                if not keys:
+                    continue
+                s = {}
+                for j in keys:
+                    acc = 0.0
+                    for d in range(D):
+                        acc += float(q[b, h, i, d]) * float(k[b, h // g, j, d])
+                    s[j] = scale * acc
+                mx = max(s.values())
+                w = {j: math.exp(s[j] - mx) for j in keys}
+                den = sum(w.values())
+                for e in range(v.shape[3]):
+                    o[b, h, i, e] = sum(w[j] * float(v[b, h // g, j, e]) for j in keys) / den
+    return o
+
+
+TINY_CASES = [
+    # B, Hq, Hkv, Sq, Sk, D, causal
+    (1, 1, 1, 5, 5, 3, True),
+    (2, 4, 2, 7, 7, 8, True),
+    (1, 4, 1, 6, 13, 4, True),    # ragged, bottom-right
+    (1, 2, 2, 17, 9, 5, True),    # Sq > Sk: first rows have no key
+    (2, 2, 1, 9, 11, 8, False),
+    (1, 3, 3, 1, 16, 8, True),    # single row
+]
+
+
+@pytest.mark.parametrize("case", TINY_CASES)
+def test_brute_force_tiny(case):
+    B, Hq, Hkv, Sq, Sk, D, causal = case
+    q, k, v = rnd((B, Hq, Sq, D), 1), rnd((B, Hkv, Sk, D), 2), rnd((B, Hkv, Sk, D), 3)
+    scale = 0.7 / math.sqrt(D)
+    got = oracle.attention_ref(q, k, v, causal, scale, row_chunk=4)
+    want = brute(q, k, v, causal, scale)
+    np.testing.assert_allclose(got, want, rtol=0, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# an independent library routine: torch's float64 CPU attention
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("case", [(2, 4, 2, 40, 40, 16, True), (1, 6, 3, 23, 71, 32, True),
+                                  (1, 2, 1, 64, 48, 64, False), (2, 8, 1, 33, 33, 128, True)])
+def test_against_torch_sdpa_float64(case):
+    B, Hq, Hkv, Sq, Sk, D, causal = case
+    q, k, v = rnd((B, Hq, Sq, D), 11), rnd((B, Hkv, Sk, D), 12), rnd((B, Hkv, Sk, D), 13)
+    scale = 1.0 / math.sqrt(D)
+    got = oracle.attention_ref(q, k, v, causal, scale)
+    g = Hq // Hkv
+    tq = torch.from_numpy(q)
+    tk = torch.from_numpy(k).repeat_interleave(g, dim=1)
+    tv = torch.from_numpy(v).repeat_interleave(g, dim=1)
+    i = torch.arange(Sq)[:, None]
+    j = torch.arange(Sk)[None, :]
+    mask = (j <= i + (Sk - Sq)) if causal else torch.ones(Sq, Sk, dtype=torch.bool)
+    want = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask,
+                                                            scale=scale).numpy()
+    rows_ok = mask.any(dim=1).numpy()
+    np.testing.assert_allclose(got[:, :, rows_ok], want[:, :, rows_ok], rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# closed forms
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("Sq,Sk", [(37, 37), (20, 50)])
+def test_identical_keys_give_prefix_mean(Sq, Sk):
+    D = 8
+    q = rnd((1, 2, Sq, D), 21)
+    krow = rnd((D,), 22)
+    k = np.broadcast_to(krow, (1, 1, Sk, D)).copy()
+    v = rnd((1, 1, Sk, D), 23)
+    got = oracle.attention_ref(q, k, v, True, 0.3)
+    csum = np.cumsum(v[0, 0], axis=0)
+    for i in range(Sq):
+        last = i + Sk - Sq
+        want = csum[last] / (last + 1)
+        np.testing.assert_allclose(got[0, :, i], np.broadcast_to(want, (2, D)), atol=1e-12)
+    # non-causal: the plain mean of all rows
+    got = oracle.attention_ref(q, k, v, False, 0.3)
+    np.testing.assert_allclose(got[0, 0], np.broadcast_to(v[0, 0].mean(0), (Sq, D)), atol=1e-12)
+
+
+def test_one_hot_dominant_key():
+    # query i points along axis i; only key j*(i) <= i has a component there,
+    # so s_{i,j*} = 60 and every other admissible score is 0 (gap 60 nats)
+    S = 64
+    rng = np.random.default_rng(31)
+    jstars = [(i * 5 + 3) % (i + 1) for i in range(S)]
+    qa = 60.0 * np.eye(S)
+    ka = np.zeros((S, S))
+    for i, js in enumerate(jstars):
+        ka[js, i] = 1.0
+    vv = rng.standard_normal((1, 1, S, 8))
+    got = oracle.attention_ref(qa[None, None], ka[None, None], vv, True, 1.0)
+    for i, js in enumerate(jstars):
+        np.testing.assert_allclose(got[0, 0, i], vv[0, 0, js], atol=1e-12)
+
+
+def test_causal_row0_is_v0_exactly():
+    q, k, v = rnd((2, 4, 19, 8), 41), rnd((2, 2, 19, 8), 42), rnd((2, 2, 19, 8), 43)
+    got = oracle.attention_ref(q, k, v, True, 0.5)
+    for h in range(4):
+        assert np.array_equal(got[:, h, 0], v[:, h // 2, 0])
+
+
+def test_probability_rows_sum_to_one_and_constant_v():
+    q, k = rnd((9, 8), 51), rnd((30, 8), 52)
+    allowed = oracle.admissible_mask(9, 30, True)
+    p = oracle.probs_ref(q, k, allowed, 0.4)
+    assert np.all(p >= 0)
+    assert np.all(p[~allowed] == 0)
+    np.testing.assert_allclose(p.sum(axis=1), 1.0, rtol=0, atol=1e-15)
+    v = np.ones((1, 1, 30, 4))
+    o = oracle.attention_ref(q[None, None], k[None, None], v, True, 0.4)
+    np.testing.assert_allclose(o, 1.0, atol=1e-15)
+
+
+def test_rows_without_keys_are_zero():
+    q, k, v = rnd((1, 1, 10, 4), 61), rnd((1, 1, 4, 4), 62), rnd((1, 1, 4, 4), 63)
+    o = oracle.attention_ref(q, k, v, True, 1.0)
+    # j <= i + (4 - 10): rows 0..5 admit nothing
+    assert np.all(o[0, 0, :6] == 0)
+    assert np.all(np.any(o[0, 0, 6:] != 0, axis=1))
+
+
+def test_scale_enters_as_temperature():
+    # scale -> 0 turns every admissible row into the uniform mean of V
+    q, k, v = rnd((1, 1, 12, 4), 71), rnd((1, 1, 12, 4), 72), rnd((1, 1, 12, 4), 73)
+    o = oracle.attention_ref(q, k, v, True, 0.0)
+    csum = np.cumsum(v[0, 0], axis=0) / np.arange(1, 13)[:, None]
+    np.testing.assert_allclose(o[0, 0], csum, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# invariants
+# ----------------------------------------------------------------------------
+def test_gqa_equals_mha_with_repeated_heads():
+    B, Hq, Hkv, S, D = 2, 8, 2, 21, 16
+    q, k, v = rnd((B, Hq, S, D), 81), rnd((B, Hkv, S, D), 82), rnd((B, Hkv, S, D), 83)
+    g = oracle.attention_ref(q, k, v, True, 0.25)
+    m = oracle.attention_ref(q, np.repeat(k, Hq // Hkv, axis=1), np.repeat(v, Hq // Hkv, axis=1),
+                             True, 0.25)
+    assert np.array_equal(g, m)
+    # and the grouping is contiguous (head h reads kv head h // 4), not strided
+    wrong = oracle.attention_ref(q, np.tile(k, (1, Hq // Hkv, 1, 1)),
+                                 np.tile(v, (1, Hq // Hkv, 1, 1)), True, 0.25)
+    assert not np.allclose(g, wrong)
+
+
+def test_rows_subset_matches_full():
+    q, k, v = rnd((1, 4, 50, 8), 91), rnd((1, 2, 70, 8), 92), rnd((1, 2, 70, 8), 93)
+    full = oracle.attention_ref(q, k, v, True, 0.3)
+    rows = [0, 3, 17, 49]
+    for h in range(4):
+        np.testing.assert_array_equal(oracle.attention_rows_ref(q, k, v, True, 0.3, 0, h, rows),
+                                      full[0, h, rows])
+
+
+def test_decode_equals_last_prefill_row_and_ignores_tail():
+    B, Hq, Hkv, D, cap = 2, 8, 2, 16, 40
+    rng = np.random.default_rng(101)
+    kc = rng.standard_normal((B, cap, Hkv, D))
+    vc = rng.standard_normal((B, cap, Hkv, D))
+    q = rng.standard_normal((B, Hq, D))
+    L = np.array([17, 40])
+    kc_nan, vc_nan = kc.copy(), vc.copy()
+    kc_nan[0, 17:] = np.nan
+    vc_nan[0, 17:] = np.nan
+    got = oracle.decode_ref(q, kc_nan, vc_nan, L, 0.2)
+    assert np.all(np.isfinite(got))
+    for b in range(B):
+        Lb = int(L[b])
+        kk = np.transpose(kc[b:b + 1, :Lb], (0, 2, 1, 3))  # [1, Hkv, L, D]
+        vv = np.transpose(vc[b:b + 1, :Lb], (0, 2, 1, 3))
+        # non-causal prefill over L keys with one query row
+        pre = oracle.attention_ref(q[b:b + 1, :, None, :], kk, vv, False, 0.2)[0, :, 0]
+        np.testing.assert_allclose(got[b], pre, atol=1e-13)
+        # last row of a causal prefill whose queries are arbitrary but end with q
+        qq = rng.standard_normal((1, Hq, Lb, D))
+        qq[0, :, -1] = q[b]
+        pre2 = oracle.attention_ref(qq, kk, vv, True, 0.2)[0, :, -1]
+        np.testing.assert_allclose(got[b], pre2, atol=1e-13)
+
+
+def test_decode_valid_len_clamped():
+    rng = np.random.default_rng(111)
+    kc, vc = rng.standard_normal((1, 8, 1, 4)), rng.standard_normal((1, 8, 1, 4))
+    q = rng.standard_normal((1, 2, 4))
+    assert np.all(oracle.decode_ref(q, kc, vc, [0], 1.0) == 0)
+    assert np.all(oracle.decode_ref(q, kc, vc, [-5], 1.0) == 0)
+    np.testing.assert_array_equal(oracle.decode_ref(q, kc, vc, [99], 1.0),
+                                  oracle.decode_ref(q, kc, vc, [8], 1.0))
+
+
+def test_split_merge_identity():
+    rng = np.random.default_rng(121)
+    R, S, D = 5, 97, 8
+    q, k, v = rng.standard_normal((R, D)), rng.standard_normal((S, D)), rng.standard_normal((S, D))
+    full = oracle.probs_ref(q, k, np.ones((R, S), bool), 0.9) @ v
+    for trial in range(20):
+        cuts = np.sort(rng.integers(0, S + 1, size=rng.integers(1, 9)))
+        edges = [0] + cuts.tolist() + [S]      # repeated cuts give empty chunks
+        parts = [oracle.partial_ref(q, k[a:b], v[a:b], 0.9) for a, b in zip(edges[:-1], edges[1:])]
+        np.testing.assert_allclose(oracle.merge_ref(parts), full, atol=1e-13)
+    empty = [oracle.partial_ref(q, k[:0], v[:0], 0.9)] * 3
+    assert np.all(oracle.merge_ref(empty) == 0)
+
+
+def test_lse_against_brute_force_and_torch():
+    B, Hq, Hkv, Sq, Sk, D = 1, 2, 1, 7, 11, 4
+    q, k = rnd((B, Hq, Sq, D), 131), rnd((B, Hkv, Sk, D), 132)
+    got = oracle.lse_ref(q, k, True, 0.6)
+    for h in range(Hq):
+        for i in range(Sq):
+            keys = [j for j in range(Sk) if j <= i + Sk - Sq]
+            want = math.log(sum(math.exp(0.6 * float(np.dot(q[0, h, i], k[0, 0, j])))
+                                for j in keys))
+            assert abs(got[0, h, i] - want) < 1e-12
+    s = 0.6 * torch.from_numpy(q[0]) @ torch.from_numpy(k[0, 0]).T
+    mask = torch.arange(Sk)[None, :] <= torch.arange(Sq)[:, None] + (Sk - Sq)
+    want = torch.logsumexp(s.masked_fill(~mask, -math.inf), dim=-1).numpy()
+    np.testing.assert_allclose(got[0], want, atol=1e-12)
+    # empty rows are -inf
+    q2, k2 = rnd((1, 1, 6, 4), 133), rnd((1, 1, 2, 4), 134)
+    l2 = oracle.lse_ref(q2, k2, True, 1.0)
+    assert np.all(np.isneginf(l2[0, 0, :4])) and np.all(np.isfinite(l2[0, 0, 4:]))
+
+
+# ----------------------------------------------------------------------------
+# the pages' own reproduction case (decode review): NaN tail, L = 1 -> V[0]
+# ----------------------------------------------------------------------------
+def test_golden_decode_nan_tail_case():
+    g = json.load(open(os.path.join(GOLDEN, "decode_nan_tail.json")))
+    s = wl.DecodeShape("golden", g["B"], g["Hq"], g["Hkv"], g["D"], g["capacity"])
+    kc, vc = wl.decode_cache(s, g["valid_len"], tail_bits=g["tail_bits"])
+    q = wl.decode_query(s, 77)
+    kf, vf, qf = oracle.widen(kc, "bf16"), oracle.widen(vc, "bf16"), oracle.widen(q, "bf16")
+    assert np.isnan(vf[0, g["valid_len"]:]).all()
+    o = oracle.decode_ref(qf, kf, vf, [g["valid_len"]], s.scale)
+    gqa = g["Hq"] // g["Hkv"]
+    for h in range(g["Hq"]):
+        assert np.array_equal(o[0, h], vf[0, 0, h // gqa])
+
+
+# ----------------------------------------------------------------------------
+# the pins catch plausible mistakes planted in the oracle
+# ----------------------------------------------------------------------------
+MUTATIONS = [
+    ("j <= (rows[:, None] + (Sk - Sq))", "j <= rows[:, None]"),          # top-left causal
+    ("j <= (rows[:, None] + (Sk - Sq))", "j < (rows[:, None] + (Sk - Sq))"),  # off by one
+    ("s = scale * (q_rows @ k.T)", "s = (q_rows @ k.T)"),                # dropped scale
+    ("hk = h // gqa", "hk = h % Hkv"),                                   # strided GQA
+    ("    if not causal:\n        return np.ones", "    if causal:\n        return np.ones"),  # mask off
+    ("den = w.sum(axis=1, keepdims=True)", "den = w.sum(axis=0, keepdims=True)"),  # wrong axis
+    ("out[b, h, rows] = p @ v[b, hk]", "out[b, h, rows] = p @ k[b, hk]"),  # wrong operand
+    ("return np.where(empty, 0.0, w / np.where(empty, 1.0, den))", "return w"),  # no normaliser
+]
+
+
+def _mutant(src_from, src_to):
+    path = os.path.join(os.path.dirname(oracle.__file__), "attention.py")
+    src = open(path).read()
+    assert src_from in src, src_from
+    ns = {"__name__": "oracle_mutant"}
+    exec(compile(src.replace(src_from, src_to, 1), "oracle_mutant", "exec"), ns)
+    return ns
+
+
+def _pins_pass(ns):
+    """A compact rerun of the brute-force and closed-form pins on a mutant."""
+    try:
+        for case in TINY_CASES[:5]:
+            B, Hq, Hkv, Sq, Sk, D, causal = case
+            q, k, v = rnd((B, Hq, Sq, D), 1), rnd((B, Hkv, Sk, D), 2), rnd((B, Hkv, Sk, D), 3)
+            scale = 0.7 / math.sqrt(D)
+            got = ns["attention_ref"](q, k, v, causal, scale, row_chunk=4)
+            if not np.allclose(got, brute(q, k, v, causal, scale), atol=1e-12, rtol=0):
+                return False
+        return True
+    except Exception:
+        return False
+
+
+def test_unmutated_oracle_passes_compact_pins():
+    assert _pins_pass(_mutant("", ""))
+
+
+@pytest.mark.parametrize("mutation", MUTATIONS, ids=[m[1][:30] for m in MUTATIONS])
+def test_planted_mistake_is_caught(mutation):
+    assert not _pins_pass(_mutant(*mutation))
