@@ -1,0 +1,151 @@
+"""MI355X (gfx950) dense flash-attention forward and Sq=1 decode.
+
+Thin Python binding over libfa.so: it checks tensors, then passes device
+pointers and torch's current HIP stream through the C ABI (include/fa.h).
+Every step of the computation runs in the library's HIP kernels; there is no
+other code path.
+
+    fwd(q, k, v, causal=..., scale=...)         -> o           (and lse on request)
+    decode(q, kcache, vcache, valid_len, ...)   -> o
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+
+from ._lib import (FA_BF16, FA_FP16, FaError, FwdPlan, check, lib)  # noqa: F401
+
+__all__ = ["fwd", "decode", "fwd_plan", "decode_workspace_bytes", "DecodeWorkspace", "FaError",
+           "lib", "build"]
+
+
+def build(verbose: bool = False) -> str:
+    from .build import build as _b
+    return _b(verbose=verbose)
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t) -> int:
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return FA_BF16
+    if t.dtype == torch.float16:
+        return FA_FP16
+    raise TypeError(f"unsupported dtype {t.dtype}; expected bfloat16 or float16")
+
+
+def _stream_ptr(t) -> int:
+    torch = _torch()
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _check_tensor(name, t, shape, dtype, device):
+    if t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, return_lse=False):
+    """Dense attention forward: q [B,Hq,Sq,D], k/v [B,Hkv,Sk,D] -> o [B,Hq,Sq,D].
+
+    Bottom-right aligned causal mask when causal=True.  scale defaults to
+    1/sqrt(D).  With return_lse=True also returns the fp32 row log-sum-exp
+    [B,Hq,Sq]."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k, v must be 4-D [B, H, S, D]")
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("fwd needs GPU tensors")
+    _check_tensor("k", k, (B, Hkv, Sk, D), q.dtype, dev)
+    _check_tensor("v", v, (B, Hkv, Sk, D), q.dtype, dev)
+    _check_tensor("q", q, (B, Hq, Sq, D), q.dtype, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, (B, Hq, Sq, D), q.dtype, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    dt = _dtype_code(q)
+    stream = _stream_ptr(q)
+    if return_lse:
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
+        st = lib().fa_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                              lse.data_ptr(), B, Hq, Hkv, Sq, Sk, D, int(bool(causal)),
+                              float(scale), dt, stream)
+        check(st, "fa_fwd_lse")
+        return out, lse
+    st = lib().fa_fwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(), B, Hq, Hkv, Sq,
+                      Sk, D, int(bool(causal)), float(scale), dt, stream)
+    check(st, "fa_fwd")
+    return out
+
+
+def fwd_plan(B, Hq, Hkv, Sq, Sk, D, causal) -> dict:
+    """The launch plan fa_fwd uses for these sizes (host only)."""
+    plan = FwdPlan()
+    check(lib().fa_fwd_plan(B, Hq, Hkv, Sq, Sk, D, int(bool(causal)), ctypes.byref(plan)),
+          "fa_fwd_plan")
+    return {f: getattr(plan, f) for f, _ in FwdPlan._fields_}
+
+
+def decode_workspace_bytes(B, Hq, Hkv, D, capacity) -> int:
+    return int(lib().fa_decode_workspace_bytes(B, Hq, Hkv, D, capacity))
+
+
+class DecodeWorkspace:
+    """Zero-filled device workspace for decode, reusable call after call on
+    one stream (each call leaves its ticket counters at zero)."""
+
+    def __init__(self, B, Hq, Hkv, D, capacity, device="cuda"):
+        torch = _torch()
+        n = decode_workspace_bytes(B, Hq, Hkv, D, capacity)
+        if n == 0:
+            raise ValueError("invalid decode sizes")
+        self.key = (B, Hq, Hkv, D, capacity)
+        self.nbytes = n
+        self.buf = torch.zeros(n + 256, dtype=torch.uint8, device=device)
+        off = (-self.buf.data_ptr()) % 256
+        self.ptr = self.buf.data_ptr() + off
+
+
+def decode(q, kcache, vcache, valid_len, causal: bool = False, scale: float | None = None,
+           out=None, workspace: DecodeWorkspace | None = None):
+    """Sq=1 attention: q [B,Hq,D] over kcache/vcache [B,capacity,Hkv,D] with
+    valid_len int32[B] on the device -> o [B,Hq,D]."""
+    torch = _torch()
+    if q.dim() != 3 or kcache.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and the caches [B, capacity, Hkv, D]")
+    B, Hq, D = q.shape
+    cap, Hkv = kcache.shape[1], kcache.shape[2]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("decode needs GPU tensors")
+    _check_tensor("q", q, (B, Hq, D), q.dtype, dev)
+    _check_tensor("kcache", kcache, (B, cap, Hkv, D), q.dtype, dev)
+    _check_tensor("vcache", vcache, (B, cap, Hkv, D), q.dtype, dev)
+    _check_tensor("valid_len", valid_len, (B,), torch.int32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, (B, Hq, D), q.dtype, dev)
+    if workspace is None:
+        workspace = DecodeWorkspace(B, Hq, Hkv, D, cap, device=dev)
+    if workspace.key != (B, Hq, Hkv, D, cap):
+        raise ValueError("workspace was sized for other shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = lib().fa_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), valid_len.data_ptr(),
+                         cap, out.data_ptr(), B, Hq, Hkv, D, int(bool(causal)), float(scale),
+                         _dtype_code(q), workspace.ptr, workspace.nbytes, _stream_ptr(q))
+    check(st, "fa_decode")
+    return out

@@ -1,0 +1,258 @@
+// C-ABI front end: argument checks (all before any HIP call), the prefill
+// launch plan, and dispatch to the gfx950 kernels.
+#include "../../include/fa.h"
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "fa_internal.h"
+
+namespace {
+
+constexpr double kLog2e = 1.442695040888963407359924681001892137;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// n = a*b*c*d elements with overflow detection (all factors >= 0)
+bool mul_ok(long long a, long long b, long long* out) {
+  if (a == 0 || b == 0) {
+    *out = 0;
+    return true;
+  }
+  if (a > LLONG_MAX / b) return false;
+  *out = a * b;
+  return true;
+}
+bool count4(long long a, long long b, long long c, long long d, long long* n) {
+  long long t;
+  return mul_ok(a, b, &t) && mul_ok(t, c, &t) && mul_ok(t, d, n);
+}
+
+bool overlaps(const void* a, long long abytes, const void* b, long long bbytes) {
+  if (!a || !b || abytes <= 0 || bbytes <= 0) return false;
+  const uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + (uintptr_t)bbytes && b0 < a0 + (uintptr_t)abytes;
+}
+
+// scale -> (|scale| * log2 e, sign applied to q in registers).  A zero scale
+// makes every admissible score 0: q is zeroed and c = 1.
+void fold_scale(float scale, float* c, int* q_sign) {
+  if (scale == 0.f) {
+    *c = 1.f;
+    *q_sign = 0;
+  } else {
+    *c = (float)(std::fabs((double)scale) * kLog2e);
+    *q_sign = scale < 0.f ? -1 : 1;
+  }
+}
+
+// Optional overrides for A/B experiments; unset means automatic.
+int env_choice(const char* name) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return -1;
+  if (!std::strcmp(v, "on") || !std::strcmp(v, "hkv") || !std::strcmp(v, "1")) return 1;
+  if (!std::strcmp(v, "off") || !std::strcmp(v, "qb") || !std::strcmp(v, "0")) return 0;
+  return -1;
+}
+
+fa_status_t plan_prefill(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
+                         fa_fwd_plan_t* plan) {
+  if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  const int BM = fa::kPrefillBM, BN = fa::kPrefillBN;
+  const long long nqb = ((long long)Sq + BM - 1) / BM;
+  long long items;
+  if (!count4(nqb, Hq, B, 1, &items) || items > INT_MAX) return FA_ERR_SHAPE;
+  std::memset(plan, 0, sizeof(*plan));
+  plan->block_m = BM;
+  plan->block_n = BN;
+  plan->work_items = (int)items;
+  const int NP = fa::kPersistentCTAs;
+  // persistent grid-stride once there are at least as many items as CTAs
+  // (page "Dense flash-attention prefill": dense_persistent="auto")
+  int persistent = items >= NP ? 1 : 0;
+  const int ep = env_choice("FA_PREFILL_PERSISTENT");
+  if (ep >= 0) persistent = ep;
+  plan->persistent = persistent;
+  plan->grid = persistent ? (int)(items < NP ? items : NP) : (int)items;
+  // kv-head-major order when GQA and gqa*NQB*B >= 2*NP, else query-block-major
+  const long long gqa = Hq / Hkv;
+  int hkv = (persistent && gqa > 1 && gqa * nqb * B >= 2LL * NP) ? 1 : 0;
+  const int eo = env_choice("FA_PREFILL_ORDER");
+  if (eo >= 0) hkv = eo;
+  plan->hkv_major = hkv;
+  // tiles streamed and tiles needing the mask, per query block (x Hq*B)
+  long long tiles = 0, masked = 0;
+  const long long off = (long long)Sk - Sq;
+  for (long long qb = 0; qb < nqb; ++qb) {
+    const long long q0 = qb * BM;
+    const long long qlast = (q0 + BM < Sq ? q0 + BM : Sq);  // one past the last row
+    long long kv_end = Sk;
+    long long free_t = Sk / BN;
+    if (causal) {
+      kv_end = qlast + off;
+      if (kv_end < 0) kv_end = 0;
+      if (kv_end > Sk) kv_end = Sk;
+      long long f = q0 + off + 1;
+      if (f < 0) f = 0;
+      f /= BN;
+      if (f < free_t) free_t = f;
+    }
+    const long long nt = (kv_end + BN - 1) / BN;
+    tiles += nt;
+    masked += nt > free_t ? nt - free_t : 0;
+  }
+  plan->kv_tiles = tiles * Hq * (long long)B;
+  plan->masked_tiles = masked * Hq * (long long)B;
+  return FA_OK;
+}
+
+fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                     int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale, int dtype,
+                     void* stream) {
+  fa_fwd_plan_t plan;
+  const fa_status_t ps = plan_prefill(B, Hq, Hkv, Sq, Sk, D, causal, &plan);
+  if (ps != FA_OK) return ps;
+  if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  long long nq, nkv, nlse;
+  if (!count4(B, Hq, Sq, D, &nq) || !count4(B, Hkv, Sk, D, &nkv) || !count4(B, Hq, Sq, 1, &nlse))
+    return FA_ERR_SHAPE;
+  if (nq > LLONG_MAX / 2 || nkv > LLONG_MAX / 2 || nlse > LLONG_MAX / 4) return FA_ERR_SHAPE;
+  // pointers may be NULL only for empty tensors
+  if (nq > 0 && (!q || !o)) return FA_ERR_NULL;
+  if (nkv > 0 && (!k || !v)) return FA_ERR_NULL;
+  for (const void* ptr : {q, k, v, static_cast<const void*>(o), static_cast<const void*>(lse)})
+    if (ptr && !aligned16(ptr)) return FA_ERR_ALIGN;
+  const long long ob = nq * 2, kb = nkv * 2;
+  if (overlaps(o, ob, q, ob) || overlaps(o, ob, k, kb) || overlaps(o, ob, v, kb))
+    return FA_ERR_ALIAS;
+  if (lse && (overlaps(lse, nlse * 4, q, ob) || overlaps(lse, nlse * 4, k, kb) ||
+              overlaps(lse, nlse * 4, v, kb) || overlaps(lse, nlse * 4, o, ob)))
+    return FA_ERR_ALIAS;
+  if (nq == 0) return FA_OK;  // nothing to compute
+
+  fa::PrefillParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.q_bstride = (long long)Hq * Sq * D;
+  p.kv_bstride = (long long)Hkv * Sk * D;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.gqa = Hq / Hkv;
+  p.kv_off = Sk - Sq;
+  p.nqb = (Sq + fa::kPrefillBM - 1) / fa::kPrefillBM;
+  p.work_items = plan.work_items;
+  p.hkv_major = plan.hkv_major;
+  p.persistent = plan.persistent;
+  fold_scale(scale, &p.c_log2, &p.q_sign);
+  const hipError_t e = fa::launch_prefill(p, D, dtype, causal != 0, plan.grid,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+                   int Sq, int Sk, int D, int causal, float scale, int dtype, void* stream) {
+  return fwd_impl(q, k, v, o, nullptr, B, Hq, Hkv, Sq, Sk, D, causal, scale, dtype, stream);
+}
+
+fa_status_t fa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                       int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
+                       int dtype, void* stream) {
+  long long nlse;
+  if (B >= 0 && Hq >= 1 && Sq >= 0 && count4(B, Hq, Sq, 1, &nlse) && nlse > 0 && !lse)
+    return FA_ERR_NULL;
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, dtype, stream);
+}
+
+fa_status_t fa_fwd_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
+                        fa_fwd_plan_t* plan) {
+  if (!plan) return FA_ERR_NULL;
+  return plan_prefill(B, Hq, Hkv, Sq, Sk, D, causal, plan);
+}
+
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int capacity) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || (D != 64 && D != 128) || capacity < 1) return 0;
+  return fa::decode_workspace_layout(B, Hq, Hkv, D, capacity, nullptr, nullptr);
+}
+
+fa_status_t fa_decode(const void* q, const void* kcache, const void* vcache,
+                      const int32_t* valid_len, int capacity, void* o, int B, int Hq, int Hkv,
+                      int D, int causal, float scale, int dtype, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  (void)causal;  // at Sq = 1 the bottom-right causal mask admits every valid token
+  if (B < 0 || Hq < 1 || Hkv < 1 || capacity < 1) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  long long nq, ncache;
+  if (!count4(B, Hq, D, 1, &nq) || !count4(B, capacity, Hkv, D, &ncache)) return FA_ERR_SHAPE;
+  if (ncache > LLONG_MAX / 2 || (long long)B * Hkv > INT_MAX / 64) return FA_ERR_SHAPE;
+  if (B == 0) return FA_OK;
+  if (!q || !kcache || !vcache || !valid_len || !o) return FA_ERR_NULL;
+  for (const void* ptr : {q, kcache, vcache, static_cast<const void*>(o)})
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(valid_len) & 3u) != 0) return FA_ERR_ALIGN;
+  const size_t need = fa::decode_workspace_layout(B, Hq, Hkv, D, capacity, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return FA_ERR_WORKSPACE;
+  const long long ob = nq * 2, cb = ncache * 2;
+  if (overlaps(o, ob, q, ob) || overlaps(o, ob, kcache, cb) || overlaps(o, ob, vcache, cb) ||
+      overlaps(o, ob, valid_len, (long long)B * 4) || overlaps(o, ob, workspace, (long long)need))
+    return FA_ERR_ALIAS;
+
+  fa::DecodeParams p;
+  p.q = q;
+  p.k = kcache;
+  p.v = vcache;
+  p.valid_len = valid_len;
+  p.o = o;
+  size_t off_ml = 0, off_tickets = 0;
+  fa::decode_workspace_layout(B, Hq, Hkv, D, capacity, &off_ml, &off_tickets);
+  char* ws = static_cast<char*>(workspace);
+  p.part_o = reinterpret_cast<float*>(ws);
+  p.part_ml = reinterpret_cast<float*>(ws + off_ml);
+  p.tickets = reinterpret_cast<unsigned*>(ws + off_tickets);
+  p.gqa = Hq / Hkv;
+  p.nsplit = fa::decode_num_splits(B, Hkv, capacity);
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.capacity = capacity;
+  fold_scale(scale, &p.c_log2, &p.q_sign);
+  const hipError_t e = fa::launch_decode(p, D, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_NULL: return "FA_ERR_NULL: a required pointer is NULL";
+    case FA_ERR_SHAPE: return "FA_ERR_SHAPE: invalid or overflowing sizes";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head_dim must be 64 or 128, dtype bf16 or fp16";
+    case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned";
+    case FA_ERR_SCALE: return "FA_ERR_SCALE: scale is not finite";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime refused the launch";
+    case FA_ERR_ALIAS: return "FA_ERR_ALIAS: the output overlaps an input";
+    default: return "unknown fa status";
+  }
+}
+
+}  // extern "C"

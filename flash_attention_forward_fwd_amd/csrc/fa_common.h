@@ -1,0 +1,105 @@
+// Device helpers shared by the gfx950 attention kernels: vector types, the
+// bf16/fp16 MFMA and pack selection, LDS transposing reads, lane exchange.
+//
+// gfx950 facts these helpers rely on (checked on the device by a layout test):
+//  * v_mfma_f32_32x32x16_{bf16,f16}: A operand lane l holds A[m = l%32][k = 8*(l/32) + e],
+//    B operand lane l holds B[k = 8*(l/32) + e][n = l%32] (e = 0..7), and the
+//    accumulator register r of lane l is C[m = 8*(r/4) + 4*(l/32) + r%4][n = l%32].
+//  * ds_read_b64_tr_b16: inside each group of 16 lanes, lanes 4e..4e+3 each
+//    name 4 consecutive 16-bit elements of "row e" (lane 4e+q the columns
+//    4q..4q+3) and lane i of the group receives column i of rows 0..3.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+
+enum : int { kBF16 = 0, kFP16 = 1 };
+
+template <int DT>
+struct Elt;
+
+template <>
+struct Elt<kBF16> {
+  // C += A * B on the 32x32x16 bf16 matrix core, fp32 accumulate.
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  // two fp32 -> packed pair, round to nearest even (v_cvt_pk_bf16_f32)
+  static __device__ __forceinline__ unsigned pack2(float lo, float hi) {
+    bf16x2 r;
+    r[0] = (__bf16)lo;
+    r[1] = (__bf16)hi;
+    return __builtin_bit_cast(unsigned, r);
+  }
+  static __device__ __forceinline__ float widen(unsigned short bits) {
+    return __uint_as_float(((unsigned)bits) << 16);
+  }
+};
+
+template <>
+struct Elt<kFP16> {
+  static __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ unsigned pack2(float lo, float hi) {
+    f16x2 r;
+    r[0] = (_Float16)lo;
+    r[1] = (_Float16)hi;
+    return __builtin_bit_cast(unsigned, r);
+  }
+  static __device__ __forceinline__ float widen(unsigned short bits) {
+    return (float)__builtin_bit_cast(_Float16, bits);
+  }
+};
+
+// 16-byte global load / store (global_load_dwordx4 / global_store_dwordx4).
+__device__ __forceinline__ u32x4 gload16(const uint16_t* p) {
+  return *reinterpret_cast<const u32x4*>(p);
+}
+
+// Transposing 64-bit LDS read (see the lane mapping above).
+__device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds) {
+  i16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) i16x4*)(lds));
+  return __builtin_bit_cast(u32x2, t);
+}
+
+__device__ __forceinline__ u32x4 lds_read16(const uint16_t* lds) {
+  return *reinterpret_cast<const u32x4*>(lds);
+}
+
+__device__ __forceinline__ void lds_write16(uint16_t* lds, u32x4 v) {
+  *reinterpret_cast<u32x4*>(lds) = v;
+}
+
+// max / sum of a value with the same value in lane l ^ 32 (v_permlane32_swap).
+__device__ __forceinline__ float pair_max(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+__device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
+constexpr float kLn2 = 0.693147180559945309417232121458f;
+
+}  // namespace fa

@@ -1,0 +1,72 @@
+// Internal interface between the C-ABI front end (fa_api.cpp) and the HIP
+// kernels (fa_prefill.hip, fa_decode.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+// ---------------------------------------------------------------------------
+// Prefill (dense forward)
+// ---------------------------------------------------------------------------
+constexpr int kPrefillWaves = 8;                 // waves per workgroup
+constexpr int kPrefillBM = 32 * kPrefillWaves;   // query rows per work item
+constexpr int kPrefillBN = 64;                   // keys per KV tile
+constexpr int kNumCUs = 256;                     // MI355X compute units
+constexpr int kPersistentCTAs = kNumCUs;         // one 8-wave workgroup per CU
+
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;          // nullptr unless the LSE variant runs
+  long long q_bstride; // elements between batches of q / o  (Hq * Sq * D)
+  long long kv_bstride;// elements between batches of k / v  (Hkv * Sk * D)
+  int B, Hq, Hkv, Sq, Sk;
+  int gqa;             // Hq / Hkv
+  int kv_off;          // Sk - Sq (bottom-right causal offset)
+  int nqb;             // ceil(Sq / BM)
+  int work_items;      // nqb * Hq * B
+  int hkv_major;       // work-item order
+  int persistent;      // grid-stride over work items
+  float c_log2;        // |scale| * log2(e), or 1 when scale == 0
+  int q_sign;          // +1, -1, or 0 (scale == 0): applied to q in registers
+};
+
+hipError_t launch_prefill(const PrefillParams& p, int D, int dtype, bool causal, int grid,
+                          hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// Decode (Sq = 1, split-KV with an in-launch merge)
+// ---------------------------------------------------------------------------
+constexpr int kDecodeWaves = 4;
+constexpr int kDecodeChunk = 32;       // tokens per MFMA step
+constexpr int kDecodeMaxGqa = 32;      // query heads sharing one kv head (MFMA N)
+
+struct DecodeParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* valid_len;
+  void* o;
+  float* part_o;       // [B*Hkv][nsplit][gqa][D] fp32
+  float* part_ml;      // [B*Hkv][nsplit][gqa][2] fp32 (m in log2 domain, l)
+  unsigned* tickets;   // [B*Hkv]
+  int B, Hq, Hkv, capacity;
+  int gqa;
+  int nsplit;          // splits per (b, kv head)
+  float c_log2;
+  int q_sign;
+};
+
+int decode_num_splits(int B, int Hkv, int capacity);
+// Workspace layout: part_o at offset 0, part_ml at *off_ml, tickets at
+// *off_tickets (either pointer may be null); returns the total size.
+size_t decode_workspace_layout(int B, int Hq, int Hkv, int D, int capacity, size_t* off_ml,
+                               size_t* off_tickets);
+hipError_t launch_decode(const DecodeParams& p, int D, int dtype, hipStream_t stream);
+
+}  // namespace fa

@@ -1,0 +1,150 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) dense flash-attention forward library.
+ *
+ * Two operations, both from the pages:
+ *
+ *  fa_fwd     Dense attention forward ("prefill"):
+ *               O = softmax(scale * Q K^T + mask) V
+ *             computed tile by tile with a running max / running sum, so the
+ *             Sq x Sk score matrix never reaches memory.  Forward only,
+ *             bf16 or fp16 storage, head_dim 64 or 128, MHA or GQA.
+ *             Page "Dense flash-attention prefill (gfx950 / MI355X)", intro
+ *             and "Baked-in levers"; tessera PR page, flash_attn forward
+ *             commit (S = scale*Q@K^T, causal/ragged mask, online softmax,
+ *             O += P@V).  Causal masking is bottom-right aligned: key j is
+ *             admissible for query i iff j <= i + (Sk - Sq) (decode PR page,
+ *             PR description: "bottom-right causal").  A query row with no
+ *             admissible key (causal with Sq > Sk, or Sk = 0) gets O = 0.
+ *
+ *  fa_decode  The Sq = 1 case over a contiguous token-major KV cache whose
+ *             valid length lives on the device and is never read by the host
+ *             (decode PR page, PR description: "device INT32 valid-length
+ *             scalar", "contiguous token-major KV").  Cache entries at or past
+ *             the valid length are never read, so NaN or garbage there cannot
+ *             reach O (decode PR page, review: unused V-cache NaNs must not
+ *             contaminate the output).  Split-KV partials are merged inside
+ *             the same launch.
+ *
+ * Conventions shared by every entry point
+ *  - All tensor pointers are device pointers owned by the caller, contiguous,
+ *    16-byte aligned, in the element type given by `dtype`.  The library never
+ *    allocates, frees or synchronises, and never reads device memory on the
+ *    host.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Work is enqueued
+ *    asynchronously on it; the call returns once enqueued.
+ *  - Every argument check runs before any HIP call, so a rejected call has no
+ *    side effect.  Launch failures are reported as FA_ERR_HIP.
+ *  - `o` must not overlap any input.
+ *  - Accumulation is fp32; P is rounded to the input type before the P*V
+ *    product; O is rounded to the output type with round-to-nearest-even.
+ */
+#ifndef FA_H_
+#define FA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FA_BF16 = 0, /* bfloat16 storage */
+  FA_FP16 = 1  /* IEEE binary16 storage */
+} fa_dtype_t;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_NULL = 1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = 2,       /* negative size, Hq % Hkv != 0, capacity < 1, size overflow */
+  FA_ERR_UNSUPPORTED = 3, /* head_dim not 64/128, dtype not bf16/fp16 */
+  FA_ERR_ALIGN = 4,       /* a tensor pointer is not 16-byte aligned */
+  FA_ERR_SCALE = 5,       /* scale is NaN or infinite */
+  FA_ERR_WORKSPACE = 6,   /* workspace NULL, misaligned or smaller than required */
+  FA_ERR_HIP = 7,         /* the HIP runtime refused the launch */
+  FA_ERR_ALIAS = 8        /* the output overlaps an input */
+} fa_status_t;
+
+/*
+ * fa_fwd -- dense attention forward.
+ *   q : [B, Hq,  Sq, D]   queries
+ *   k : [B, Hkv, Sk, D]   keys
+ *   v : [B, Hkv, Sk, D]   values
+ *   o : [B, Hq,  Sq, D]   output (written)
+ * Query head h reads kv head h / (Hq / Hkv) (contiguous GQA groups).
+ * causal != 0 selects the bottom-right aligned causal mask.
+ * scale multiplies the q.k dot products (1/sqrt(D) is the usual value).
+ * B, Sq or Sk may be 0: B = 0 or Sq = 0 enqueues nothing; Sk = 0 writes O = 0.
+ */
+fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o,
+                   int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                   int causal, float scale, int dtype, void* stream);
+
+/*
+ * fa_fwd_lse -- fa_fwd that also writes the natural-log row log-sum-exp
+ *   lse : [B, Hq, Sq] float32, lse[b,h,i] = log sum_{j admissible} exp(scale*q_i.k_j),
+ *         -inf for a row with no admissible key.
+ * The per-row running max and running sum of the online softmax give it for
+ * free; it is the quantity a split or cross-device merge of partial outputs
+ * needs (decode PR page lists LSE as a follow-up; the tessera backward uses
+ * it as L).
+ */
+fa_status_t fa_fwd_lse(const void* q, const void* k, const void* v, void* o, float* lse,
+                       int B, int Hq, int Hkv, int Sq, int Sk, int D,
+                       int causal, float scale, int dtype, void* stream);
+
+/*
+ * fa_fwd_plan -- the launch plan fa_fwd would use for a shape (host only, no
+ * HIP call).  Exposed so the schedule can be inspected and tested.
+ */
+typedef struct {
+  int block_m;          /* query rows per work item */
+  int block_n;          /* keys per KV tile */
+  int work_items;       /* ceil(Sq / block_m) * Hq * B */
+  int grid;             /* workgroups launched */
+  int persistent;       /* 1 = grid-stride persistent launch */
+  int hkv_major;        /* 1 = work items ordered kv-head-major, 0 = query-block-major */
+  long long kv_tiles;   /* KV tiles streamed, summed over work items */
+  long long masked_tiles; /* of those, tiles that need the mask */
+} fa_fwd_plan_t;
+
+fa_status_t fa_fwd_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
+                        fa_fwd_plan_t* plan);
+
+/*
+ * fa_decode_workspace_bytes -- bytes of workspace fa_decode needs for these
+ * sizes (0 on invalid sizes).  The workspace holds fp32 split partials and
+ * one ticket counter per (batch, kv head).
+ */
+size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int capacity);
+
+/*
+ * fa_decode -- single-token (Sq = 1) attention over a KV cache.
+ *   q         : [B, Hq, D]                 query of the new token
+ *   kcache    : [B, capacity, Hkv, D]      token-major key cache
+ *   vcache    : [B, capacity, Hkv, D]      token-major value cache
+ *   valid_len : int32[B] on the device; batch b attends to tokens
+ *               [0, clamp(valid_len[b], 0, capacity)).  Never read on the host.
+ *   o         : [B, Hq, D]                 output (written); 0 when the length is 0
+ *   causal    : accepted for symmetry with fa_fwd; at Sq = 1 the bottom-right
+ *               causal mask admits every valid token, so it changes nothing.
+ *   workspace : device memory of at least fa_decode_workspace_bytes(...) bytes,
+ *               256-byte aligned, zero-filled by the caller once when it is
+ *               allocated.  Every call leaves its ticket counters at zero again,
+ *               so it can be reused call after call on one stream.  Two calls
+ *               in flight at once must not share a workspace.
+ * Tokens at or past the valid length are never loaded.
+ */
+fa_status_t fa_decode(const void* q, const void* kcache, const void* vcache,
+                      const int32_t* valid_len, int capacity, void* o,
+                      int B, int Hq, int Hkv, int D, int causal, float scale, int dtype,
+                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* Human-readable name of a status code (static storage). */
+const char* fa_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H_ */
