@@ -37,25 +37,40 @@ constexpr int kDVPad = 32;       // V staging row pad (elements)
 
 __device__ __forceinline__ int heads_in_group(int gqa, int hg) { return min(32, gqa - 32 * hg); }
 
-// Merge `n` partial records [first, first + n) of `src` into record `dst_idx`
-// of `dst` (unnormalised), or into the output when `out` is not null.
-template <int D, int DT>
+// Partials cross workgroups (and XCDs, whose L2 caches are not coherent with
+// each other) through agent-scope relaxed atomic loads and stores: they are
+// written through to the device-coherent level and read from it, so no
+// whole-cache writeback or invalidate (what a device-scope fence costs on
+// gfx950) is needed.  Ordering comes from waiting for the stores to complete
+// (vmcnt(0)) before the ticket is taken.
+__device__ __forceinline__ float ld_coherent(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_coherent(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+
+// Merge `n` partial records [first, first + n) of (src_o, src_ml) -- LDS when
+// SRC_LDS, otherwise global -- into one unnormalised record (dst_o, dst_ml) in
+// global memory, or, when `out` is not null, normalise and write O.
+template <int D, int DT, bool SRC_LDS>
 __device__ void merge_partials(const float* src_o, const float* src_ml, int first, int n, int gg,
                                float* dst_o, float* dst_ml, uint16_t* out, long long out_base,
                                float* lds_scratch) {
   using E = Elt<DT>;
-  // per head: M and the weights, computed once into LDS
-  float* w = lds_scratch;              // [gg][n] weights
+  auto ld = [](const float* p) { return SRC_LDS ? *p : ld_coherent(p); };
+  float* w = lds_scratch;              // [gg][n] weights 2^(m_s - M)
   float* den = lds_scratch + gg * n;   // [gg]
   float* Mh = den + gg;                // [gg]
   for (int g = threadIdx.x; g < gg; g += blockDim.x) {
     float M = -__builtin_inff();
-    for (int s = 0; s < n; ++s) M = fmaxf(M, src_ml[((long long)(first + s) * gg + g) * 2 + 0]);
+    for (int s = 0; s < n; ++s) M = fmaxf(M, ld(src_ml + ((long long)(first + s) * gg + g) * 2));
     const float Mu = (M == -__builtin_inff()) ? 0.f : M;
     float dsum = 0.f;
     for (int s = 0; s < n; ++s) {
-      const float m = src_ml[((long long)(first + s) * gg + g) * 2 + 0];
-      const float l = src_ml[((long long)(first + s) * gg + g) * 2 + 1];
+      const float m = ld(src_ml + ((long long)(first + s) * gg + g) * 2 + 0);
+      const float l = ld(src_ml + ((long long)(first + s) * gg + g) * 2 + 1);
       const float f = fast_exp2(m - Mu);  // m = -inf -> 0
       w[g * n + s] = f;
       dsum += f * l;
@@ -69,41 +84,41 @@ __device__ void merge_partials(const float* src_o, const float* src_ml, int firs
     float acc = 0.f;
     for (int s = 0; s < n; ++s) {
       const float f = w[g * n + s];
-      if (f != 0.f) acc += f * src_o[((long long)(first + s) * gg + g) * D + d];
+      const float x = ld(src_o + ((long long)(first + s) * gg + g) * D + d);
+      if (f != 0.f) acc += f * x;
     }
     if (out) {
       const float dd = den[g];
       const float val = dd > 0.f ? acc / dd : 0.f;
       out[out_base + (long long)g * D + d] = (uint16_t)(E::pack2(val, 0.f) & 0xFFFFu);
     } else {
-      dst_o[(long long)g * D + d] = acc;
+      st_coherent(dst_o + (long long)g * D + d, acc);
     }
   }
   if (!out) {
     for (int g = threadIdx.x; g < gg; g += blockDim.x) {
-      dst_ml[g * 2 + 0] = Mh[g];
-      dst_ml[g * 2 + 1] = den[g];
+      st_coherent(dst_ml + g * 2 + 0, Mh[g]);
+      st_coherent(dst_ml + g * 2 + 1, den[g]);
     }
   }
   __syncthreads();
 }
 
-// Workgroup-wide ticket: returns true in every thread of the workgroup that
-// arrives last (count reaches `total`), after which it resets the counter.
+// Workgroup-wide ticket after this workgroup's record is stored: true in every
+// thread of the workgroup that arrives last (count reaches `total`); that
+// workgroup also resets the counter for the next call.
 __device__ __forceinline__ bool take_ticket(unsigned* counter, unsigned total, int* lds_flag) {
-  __threadfence();  // make this thread's partial writes visible device-wide
+  wait_stores();
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned t =
-        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = (t == total - 1);
     if (last) __hip_atomic_store(counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     *lds_flag = last ? 1 : 0;
   }
   __syncthreads();
-  const bool last = *lds_flag != 0;
-  if (last) __threadfence();  // acquire: see every other workgroup's partials
-  return last;
+  return *lds_flag != 0;
 }
 
 template <int D, int DT>
@@ -270,10 +285,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(DecodeParams 
   const long long out_base = ((long long)b * p.Hq + hq0) * D;
 
   if (p.nsplit == 1) {
-    merge_partials<D, DT>(wo, wml, 0, NW, gg, nullptr, nullptr, og, out_base, scratch);
+    merge_partials<D, DT, true>(wo, wml, 0, NW, gg, nullptr, nullptr, og, out_base, scratch);
     return;
   }
-  merge_partials<D, DT>(wo, wml, 0, NW, gg, part_o + (long long)split * gg * D,
+  merge_partials<D, DT, true>(wo, wml, 0, NW, gg, part_o + (long long)split * gg * D,
                         part_ml + (long long)split * gg * 2, nullptr, 0, scratch);
 
   // ---- level 1: last workgroup of the group merges the group -------------------
@@ -283,16 +298,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(DecodeParams 
   unsigned* cnt0 = p.tickets + (long long)unit * (ngroups + 1);
   if (!take_ticket(cnt0 + grp, (unsigned)gsize, &ticket_flag)) return;
   if (ngroups == 1) {
-    merge_partials<D, DT>(part_o, part_ml, gfirst, gsize, gg, nullptr, nullptr, og, out_base,
+    merge_partials<D, DT, false>(part_o, part_ml, gfirst, gsize, gg, nullptr, nullptr, og, out_base,
                           scratch);
     return;
   }
-  merge_partials<D, DT>(part_o, part_ml, gfirst, gsize, gg,
+  merge_partials<D, DT, false>(part_o, part_ml, gfirst, gsize, gg,
                         part_o + (long long)(p.nsplit + grp) * gg * D,
                         part_ml + (long long)(p.nsplit + grp) * gg * 2, nullptr, 0, scratch);
   // ---- level 2: last group merger merges the groups and writes O -----------
   if (!take_ticket(cnt0 + ngroups, (unsigned)ngroups, &ticket_flag)) return;
-  merge_partials<D, DT>(part_o, part_ml, p.nsplit, ngroups, gg, nullptr, nullptr, og, out_base,
+  merge_partials<D, DT, false>(part_o, part_ml, p.nsplit, ngroups, gg, nullptr, nullptr, og, out_base,
                         scratch);
 }
 
