@@ -7,7 +7,10 @@ from __future__ import annotations
 import ctypes
 import os
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+# FA_LIB selects another build of the same library (A/B experiments); the
+# default is the in-tree build.
+LIB_PATH = os.environ.get("FA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                     "libfa.so")
 
 FA_OK = 0
 STATUS_NAMES = {

@@ -47,23 +47,30 @@ def _run(cmd, verbose):
         print(err)
 
 
-def build(verbose: bool = False, jobs: int | None = None) -> str:
-    """Compile every source and link libfa.so; returns the library path."""
+def build(verbose: bool = False, jobs: int | None = None, defines=(), out: str | None = None,
+          objdir: str | None = None) -> str:
+    """Compile every source and link libfa.so; returns the library path.
+
+    `defines` (e.g. ["FA_PREFILL_WAVES=4"]) and `out` build a variant of the
+    library elsewhere for A/B measurements; the default is the in-tree build."""
     cc = hipcc()
-    os.makedirs(BUILD, exist_ok=True)
+    objdir = objdir or BUILD
+    out = out or LIB
+    os.makedirs(objdir, exist_ok=True)
     objs, cmds = [], []
+    dflags = [f"-D{d}" for d in defines]
     for src in SOURCES:
-        obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
+        obj = os.path.join(objdir, os.path.splitext(src)[0] + ".o")
         objs.append(obj)
-        cmds.append([cc, *COMMON, *DEVICE_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([cc, *COMMON, *DEVICE_FLAGS, *dflags, "-c", os.path.join(CSRC, src), "-o", obj])
     jobs = jobs or min(len(cmds), max(1, (os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    tmp = LIB + ".tmp"
+    tmp = out + ".tmp"
     _run([cc, "-shared", f"--offload-arch={ARCH}", "-o", tmp, *objs], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -11,11 +11,16 @@ namespace fa {
 // ---------------------------------------------------------------------------
 // Prefill (dense forward)
 // ---------------------------------------------------------------------------
-constexpr int kPrefillWaves = 8;                 // waves per workgroup
+#ifndef FA_PREFILL_WAVES
+#define FA_PREFILL_WAVES 8
+#endif
+constexpr int kPrefillWaves = FA_PREFILL_WAVES;  // waves per workgroup, 32 query rows each
 constexpr int kPrefillBM = 32 * kPrefillWaves;   // query rows per work item
 constexpr int kPrefillBN = 64;                   // keys per KV tile
 constexpr int kNumCUs = 256;                     // MI355X compute units
-constexpr int kPersistentCTAs = kNumCUs;         // one 8-wave workgroup per CU
+// two waves per SIMD: 8 waves per CU
+constexpr int kPrefillCTAsPerCU = 8 / kPrefillWaves;
+constexpr int kPersistentCTAs = kNumCUs * kPrefillCTAsPerCU;
 
 struct PrefillParams {
   const void* q;

@@ -42,6 +42,19 @@ namespace {
 constexpr int kKPad = 8;   // K LDS row = D + 8 elements (16-byte skew per row)
 constexpr int kVPad = 32;  // V LDS row = D + 32 elements (64-byte skew per row)
 
+// The exp2 reference max of a row moves only when the row's running max
+// exceeds it by more than kRescaleTau (log2 units), so p = exp2(s*c - m_ref)
+// stays <= 2^kRescaleTau and the O accumulator is rescaled only on the rare
+// tiles where some row of the wave jumps that far.  The final O / l and the
+// LSE are exact for any reference, so this changes rounding only.
+#ifndef FA_RESCALE_TAU
+#define FA_RESCALE_TAU 8.0f
+#endif
+constexpr float kRescaleTau = FA_RESCALE_TAU;
+#ifndef FA_MFMA_SETPRIO
+#define FA_MFMA_SETPRIO 0
+#endif
+
 // Work item -> (batch, query head, query block).  Query blocks are visited
 // heaviest first (a causal block's cost grows with its index).
 __device__ __forceinline__ void decode_item(const PrefillParams& p, int w, int& b, int& hq,
@@ -197,6 +210,7 @@ void prefill_kernel(PrefillParams p) {
         const uint16_t* Vb = Vs + buf * BN * VST;
         // ---- S^T = K Q^T for keys [t*BN, t*BN + 64) --------------------------
         f32x16 s0 = f32x16{}, s1 = f32x16{};
+        if (FA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int kk = 0; kk < KSTEPS; ++kk) {
           const u32x4 a0 = lds_read16(Kb + k_lane + 16 * kk);
@@ -204,6 +218,7 @@ void prefill_kernel(PrefillParams p) {
           s0 = E::mfma(a0, qr[kk], s0);
           s1 = E::mfma(a1, qr[kk], s1);
         }
+        if (FA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(0);
         // ---- mask (diagonal / tail tiles only) -----------------------------
         if (t >= free_tiles) {
           const int kb = t * BN + 4 * lh;
@@ -224,10 +239,16 @@ void prefill_kernel(PrefillParams p) {
         float mx = fmaxf(s0[0], s1[0]);
 #pragma unroll
         for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-        mx = pair_max(mx);
-        const float m_new = fmaxf(m_run, mx * c);
-        const float m_use = (m_new == -__builtin_inff()) ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
+        mx = pair_max(mx) * c;  // this tile's row max, log2 domain
+        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleTau)) {
+          const float m_new = fmaxf(m_run, mx);
+          const float alpha = fast_exp2(m_run - ((m_new == -__builtin_inff()) ? 0.f : m_new));
+          l_run *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < DTILES; ++dt) oacc[dt] *= alpha;
+          m_run = m_new;
+        }
+        const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
         float psum = 0.f;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
@@ -235,13 +256,9 @@ void prefill_kernel(PrefillParams p) {
           s1[r] = fast_exp2(__builtin_fmaf(s1[r], c, -m_use));
           psum += s0[r] + s1[r];
         }
-        l_run = l_run * alpha + psum;
-        m_run = m_new;
-        if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
-#pragma unroll
-          for (int dt = 0; dt < DTILES; ++dt) oacc[dt] *= alpha;
-        }
+        l_run += psum;
         // ---- O^T += V^T P^T ---------------------------------------------------
+        if (FA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const f32x16& sp = st ? s1 : s0;
@@ -260,6 +277,7 @@ void prefill_kernel(PrefillParams p) {
             }
           }
         }
+        if (FA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(0);
       }
 
       if (t + 1 < ntiles) lstore_tile(buf ^ 1);
