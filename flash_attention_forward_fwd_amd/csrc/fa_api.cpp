@@ -123,6 +123,8 @@ fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
   if (!count4(B, Hq, Sq, D, &nq) || !count4(B, Hkv, Sk, D, &nkv) || !count4(B, Hq, Sq, 1, &nlse))
     return FA_ERR_SHAPE;
   if (nq > LLONG_MAX / 2 || nkv > LLONG_MAX / 2 || nlse > LLONG_MAX / 4) return FA_ERR_SHAPE;
+  // one (batch, kv head) of K or V is addressed with 32-bit byte offsets
+  if ((long long)Sk * D * 2 > INT_MAX) return FA_ERR_SHAPE;
   // pointers may be NULL only for empty tensors
   if (nq > 0 && (!q || !o)) return FA_ERR_NULL;
   if (nkv > 0 && (!k || !v)) return FA_ERR_NULL;

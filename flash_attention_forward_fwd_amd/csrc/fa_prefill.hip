@@ -33,12 +33,16 @@
 //    idea).  O^T keeps one query row per lane, so the rescale by
 //    exp2(m_old - m_new) is lane-local and is skipped when no row of the
 //    wave raised its max (x * 1.0 == x, so skipping changes no bit).
+#include <type_traits>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
 namespace fa {
 namespace {
 
+// gfx9 buffer resource word 3: 32-bit data format, raw (unswizzled) access
+constexpr int kBufferFlags = 0x00020000;
 constexpr int kKPad = 8;   // K LDS row = D + 8 elements (16-byte skew per row)
 constexpr int kVPad = 32;  // V LDS row = D + 32 elements (64-byte skew per row)
 
@@ -51,9 +55,38 @@ constexpr int kVPad = 32;  // V LDS row = D + 32 elements (64-byte skew per row)
 #define FA_RESCALE_TAU 8.0f
 #endif
 constexpr float kRescaleTau = FA_RESCALE_TAU;
+// LDS operand reads run this many MFMAs ahead of their consumer in the
+// steady-state M step (LDS latency under load exceeds two MFMAs)
+#ifndef FA_LOOKAHEAD
+#define FA_LOOKAHEAD 4
+#endif
+constexpr int kLookahead = FA_LOOKAHEAD;
 #ifndef FA_MFMA_SETPRIO
 #define FA_MFMA_SETPRIO 0
 #endif
+
+// Instruction order of a steady-state M step for the scheduler: NPV PV MFMAs
+// (each consumes two transposing V reads) then NQK QK MFMAs (each consumes
+// one 16-byte K read).  Every read is issued LA MFMAs before its consumer.
+template <int NPV, int NQK, int LA>
+struct MStepSchedule {
+  static constexpr int NM = NPV + NQK;
+  static constexpr int reads_upto(int m) { return m <= NPV ? 2 * m : 2 * NPV + (m - NPV); }
+  template <int I>
+  static __device__ __forceinline__ void emit() {
+    if constexpr (I < NM) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+      constexpr int hi = (I + LA < NM) ? reads_upto(I + LA + 1) : reads_upto(NM);
+      constexpr int lo = (I + LA - 1 < NM) ? reads_upto(I + LA) : reads_upto(NM);
+      if constexpr (hi - lo > 0) __builtin_amdgcn_sched_group_barrier(0x100, hi - lo, 0);
+      emit<I + 1>();
+    }
+  }
+  static __device__ __forceinline__ void apply() {
+    __builtin_amdgcn_sched_group_barrier(0x100, reads_upto(LA < NM ? LA : NM), 0);  // primer
+    emit<0>();
+  }
+};
 
 // Work item -> (batch, query head, query block).  Query blocks are visited
 // heaviest first (a causal block's cost grows with its index).
@@ -88,17 +121,20 @@ void prefill_kernel(PrefillParams p) {
   constexpr int NT = kPrefillWaves * 64;
   constexpr int BM = kPrefillBM;
   constexpr int BN = kPrefillBN;
+  constexpr int NBUF = 3;            // LDS ring: tiles t-1, t, t+1 live while t+2 lands
   constexpr int KST = D + kKPad;
   constexpr int VST = D + kVPad;
-  constexpr int KSTEPS = D / 16;    // k-steps of the QK product
-  constexpr int DTILES = D / 32;    // 32-wide column tiles of O
-  constexpr int CH = D / 8;         // 16-byte chunks per K/V row
-  constexpr int PER = BN * CH / NT; // chunks per thread per tile
+  constexpr int KTILE = BN * KST;    // elements per K buffer
+  constexpr int VTILE = BN * VST;    // elements per V buffer
+  constexpr int KSTEPS = D / 16;     // k-steps of the QK product
+  constexpr int DTILES = D / 32;     // 32-wide column tiles of O
+  constexpr int CH = D / 8;          // 16-byte chunks per K/V row
+  constexpr int PER = BN * CH / NT;  // chunks per thread per tile
   static_assert(BN * CH % NT == 0, "tile copy must divide evenly");
-  static_assert(BN == 64, "the softmax below assumes two 32-key S tiles");
+  static_assert(BN == 64, "a tile is two 32-key sub-tiles");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[2 * BN * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * BN * VST];
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF * KTILE];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[NBUF * VTILE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -146,9 +182,14 @@ void prefill_kernel(PrefillParams p) {
     }
     if (rw0 >= p.Sq) wave_end = 0;
     const int ntiles = (kv_end + BN - 1) / BN;
-    // tiles [0, free_tiles) are admissible for every row of this wave
-    int free_tiles = p.Sk / BN;
-    if (CAUSAL) free_tiles = min(free_tiles, max(rw0 + p.kv_off + 1, 0) / BN);
+    // tiles [0, free_tiles) are admissible for every row of this wave, tiles
+    // [0, main_tiles) for every row of the workgroup (the mask-free body)
+    int free_tiles = p.Sk / BN, main_tiles = p.Sk / BN;
+    if (CAUSAL) {
+      free_tiles = min(free_tiles, max(rw0 + p.kv_off + 1, 0) / BN);
+      main_tiles = min(main_tiles, max(q0 + p.kv_off + 1, 0) / BN);
+    }
+    main_tiles = min(main_tiles, ntiles);
 
     // Q rows of this wave as the B operand: lane holds q[row][16kk + 8lh .. +7]
     u32x4 qr[KSTEPS];
@@ -164,125 +205,243 @@ void prefill_kernel(PrefillParams p) {
     f32x16 oacc[DTILES];
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) oacc[dt] = f32x16{};
-    float m_run = -__builtin_inff();
-    float l_run = 0.f;
+    float m_run = -__builtin_inff();  // exp2 reference max (log2 domain)
+    float l_run = 0.f;                // this lane's half of the row sum
 
-    // global -> registers -> LDS staging of one KV tile
-    u32x4 kst[PER], vst[PER];
-    auto gload_tile = [&](int t) {
+    // one group (4 waves, 256 threads) copies the K or the V half of a tile
+    // global -> registers -> LDS inside its V phase; keys >= Sk become zeros
+    constexpr int GT = NT / 2;              // threads per group
+    constexpr int GPER = BN * CH / GT;      // 16-byte chunks per thread per half tile
+    static_assert(BN * CH % GT == 0, "half-tile copy must divide evenly");
+    const int gtid = tid % GT;
+    // buffer descriptors over this (batch, kv head)'s K and V: the tile offset
+    // is a scalar, the lane offset a 32-bit VGPR, and reads past Sk return 0
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kg + kvbase), (short)0, p.Sk * D * 2, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(vg + kvbase), (short)0, p.Sk * D * 2, kBufferFlags);
+    auto gload_half = [&](__amdgpu_buffer_rsrc_t rs, int t, u32x4 (&R)[GPER]) {
 #pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int cidx = tid + u * NT;
+      for (int u = 0; u < GPER; ++u) {
+        const int cidx = gtid + u * GT;
         const int rr = cidx / CH, cc = cidx % CH;
-        const int key = t * BN + rr;
-        u32x4 kx = {0u, 0u, 0u, 0u}, vx = {0u, 0u, 0u, 0u};
-        if (key < p.Sk) {
-          const long long off = kvbase + (long long)key * D + cc * 8;
-          kx = gload16(kg + off);
-          vx = gload16(vg + off);
+        R[u] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (rr * D + cc * 8) * 2, t * BN * D * 2, 0));
+      }
+    };
+    auto lstore_half = [&](uint16_t* dst, int stride, const u32x4 (&R)[GPER]) {
+#pragma unroll
+      for (int u = 0; u < GPER; ++u) {
+        const int cidx = gtid + u * GT;
+        const int rr = cidx / CH, cc = cidx % CH;
+        lds_write16(dst + rr * stride + cc * 8, R[u]);
+      }
+    };
+
+    // ---- the three stages of a 32-key sub-tile ---------------------------------
+    // A: S^T = K Q^T for keys [32 st, 32 st + 32) of the tile in buffer Kb
+    auto stage_qk = [&](const uint16_t* Kb, int st, f32x16& S) {
+      S = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        S = E::mfma(lds_read16(Kb + k_lane + 32 * st * KST + 16 * kk), qr[kk], S);
+    };
+    // B1: row max of the sub-tile (log2 domain); move the reference max and
+    // rescale O and l when some row of the wave jumped above it by > tau
+    auto stage_max = [&](const f32x16& S) {
+      float mx = fmaxf(fmaxf(S[0], S[1]), S[2]);
+#pragma unroll
+      for (int r = 3; r < 15; r += 2) mx = fmaxf(mx, fmaxf(S[r], S[r + 1]));
+      mx = fmaxf(mx, S[15]);
+      mx = pair_max(mx) * c;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleTau)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - ((m_new == -__builtin_inff()) ? 0.f : m_new));
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+      }
+    };
+    // B1 over a 64-key tile held as two S accumulators
+    auto stage_max2 = [&](const f32x16& A, const f32x16& B) {
+      float mx = fmaxf(fmaxf(A[0], A[1]), B[0]);
+#pragma unroll
+      for (int r = 2; r < 16; ++r) mx = fmaxf(fmaxf(mx, A[r]), B[r - 1]);
+      mx = fmaxf(mx, B[15]);
+      mx = pair_max(mx) * c;
+      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleTau)) {
+        const float m_new = fmaxf(m_run, mx);
+        const float alpha = fast_exp2(m_run - ((m_new == -__builtin_inff()) ? 0.f : m_new));
+        l_run *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt) oacc[dt] *= alpha;
+        m_run = m_new;
+      }
+    };
+    // B2: p = exp2(s c - m), row-sum partial, pack to the P operand
+    auto stage_exp = [&](f32x16& S, u32x4 (&P)[2]) {
+      const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
+      float psum = 0.f;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        S[r] = fast_exp2(__builtin_fmaf(S[r], c, -m_use));
+        psum += S[r];
+      }
+      l_run += psum;
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int r0 = 8 * kk;
+        P[kk] = u32x4{E::pack2(S[r0 + 0], S[r0 + 1]), E::pack2(S[r0 + 2], S[r0 + 3]),
+                      E::pack2(S[r0 + 4], S[r0 + 5]), E::pack2(S[r0 + 6], S[r0 + 7])};
+      }
+    };
+    // C: O^T += V^T P^T for keys [32 st, 32 st + 32) of the tile in buffer Vb
+    auto stage_pv = [&](const uint16_t* Vb, int st, const u32x4 (&P)[2]) {
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const uint16_t* vrow = Vb + v_lane + (32 * st + 16 * kk) * VST;
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt) {
+          const u32x2 lo = lds_read_tr16(vrow + 32 * dt);
+          const u32x2 hi = lds_read_tr16(vrow + 8 * VST + 32 * dt);
+          oacc[dt] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, P[kk], oacc[dt]);
         }
-        kst[u] = kx;
-        vst[u] = vx;
-      }
-    };
-    auto lstore_tile = [&](int buf) {
-#pragma unroll
-      for (int u = 0; u < PER; ++u) {
-        const int cidx = tid + u * NT;
-        const int rr = cidx / CH, cc = cidx % CH;
-        lds_write16(Ks + buf * BN * KST + rr * KST + cc * 8, kst[u]);
-        lds_write16(Vs + buf * BN * VST + rr * VST + cc * 8, vst[u]);
       }
     };
 
-    if (ntiles > 0) {
-      gload_tile(0);
-      lstore_tile(0);
+    // ---- ping-pong schedule ----------------------------------------------------
+    // Each wave runs the step sequence M(0) V(0) M(1) V(1) ... M(ntiles) over
+    // its 64-key tiles:
+    //   M(t): S_t = K_t Q^T, then O^T += V_{t-1}^T P_{t-1}^T   (32 MFMAs)
+    //   V(t): mask (diagonal / tail only), online softmax of S_t -> P_t
+    // The two waves that share a SIMD run the sequence one phase apart (waves
+    // 0-3 lead, 4-7 follow): while one issues MFMAs the other runs its softmax
+    // on the vector unit.  Every phase ends with a workgroup barrier.  LDS
+    // holds rings of three K and three V tiles: K(t) is read in phases 2t,
+    // 2t+1 and V(t) in 2t+2, 2t+3, so K(X) written in phase 2X-3 and V(X) in
+    // phase 2X-2 never overwrite a tile still being read.
+    // ring slot of a tile; readfirstlane keeps it a per-phase scalar instead
+    // of letting strength reduction turn every LDS address into a live
+    // induction register
+    auto slot = [](int tile) { return uniform(tile % NBUF); };
+    // tile t is needed by this wave iff t*BN < wave_end; sub-tile keys past
+    // free_keys need the mask for some row of this wave
+    int free_keys = p.Sk;
+    if (CAUSAL) free_keys = min(free_keys, max(rw0 + p.kv_off + 1, 0));
+    const int nphase = ntiles > 0 ? 2 * ntiles + 2 : 0;
+    // phases [4, main_end) run straight-line steps: every tile they touch
+    // (t-1, t with t <= main_tiles - 2 for the lagging group) is needed by
+    // every wave and mask-free
+    const int main_end = 2 * main_tiles - 2;
+
+    // prologue: the leading group copies K of tiles 0 and 1, the following V
+    {
+      const bool lead = wave < kPrefillWaves / 2;
+      u32x4 R0[GPER], R1[GPER];
+      gload_half(lead ? krs : vrs, 0, R0);
+      if (ntiles > 1) gload_half(lead ? krs : vrs, 1, R1);
+      if (lead) {
+        lstore_half(Ks, KST, R0);
+        if (ntiles > 1) lstore_half(Ks + slot(1) * KTILE, KST, R1);
+      } else {
+        lstore_half(Vs, VST, R0);
+        if (ntiles > 1) lstore_half(Vs + slot(1) * VTILE, VST, R1);
+      }
     }
     __syncthreads();
 
-    for (int t = 0; t < ntiles; ++t) {
-      const int buf = t & 1;
-      if (t + 1 < ntiles) gload_tile(t + 1);
-
-      if (t * BN < wave_end) {
-        const uint16_t* Kb = Ks + buf * BN * KST;
-        const uint16_t* Vb = Vs + buf * BN * VST;
-        // ---- S^T = K Q^T for keys [t*BN, t*BN + 64) --------------------------
-        f32x16 s0 = f32x16{}, s1 = f32x16{};
-        if (FA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          const u32x4 a0 = lds_read16(Kb + k_lane + 16 * kk);
-          const u32x4 a1 = lds_read16(Kb + k_lane + 32 * KST + 16 * kk);
-          s0 = E::mfma(a0, qr[kk], s0);
-          s1 = E::mfma(a1, qr[kk], s1);
-        }
-        if (FA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(0);
-        // ---- mask (diagonal / tail tiles only) -----------------------------
-        if (t >= free_tiles) {
-          const int kb = t * BN + 4 * lh;
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j0 = kb + 8 * (r >> 2) + (r & 3);
-            const int j1 = j0 + 32;
-            bool bad0 = j0 >= p.Sk, bad1 = j1 >= p.Sk;
-            if (CAUSAL) {
-              bad0 = bad0 || (j0 > row + p.kv_off);
-              bad1 = bad1 || (j1 > row + p.kv_off);
-            }
-            if (bad0) s0[r] = -__builtin_inff();
-            if (bad1) s1[r] = -__builtin_inff();
+    auto run = [&](auto lag_c) {
+      constexpr int LAG = decltype(lag_c)::value;
+      f32x16 S0 = f32x16{}, S1 = f32x16{};  // S of the tile between its M and V steps
+      u32x4 P0[2], P1[2];                   // P of the tile between its V and next M steps
+      auto needed = [&](int t) { return t >= 0 && t < ntiles && t * BN < wave_end; };
+      // one phase of kind KIND (0: M step, 1: V step) for this wave; ALL: every
+      // operation of the step is known to be needed and mask-free
+      auto phase = [&](int g, auto kind_c, auto all_c) {
+        constexpr int KIND = decltype(kind_c)::value;
+        constexpr bool ALL = decltype(all_c)::value;
+        // the leading group copies K(X) in its V phase 2X-3, the following
+        // group V(X) in its V phase 2X-2 (tiles 0 and 1 come with the prologue)
+        const int Xld = LAG == 0 ? (g + 3) >> 1 : (g + 2) >> 1;
+        const bool do_load = KIND == 1 && Xld >= 2 && Xld < ntiles;
+        u32x4 R[GPER];
+        if (do_load) gload_half(LAG == 0 ? krs : vrs, Xld, R);
+        const int sidx = g - LAG;
+        const int t = sidx >> 1;
+        if (KIND == 0 && ALL) {
+          // M(t), steady state: 4*DTILES PV MFMAs (P_{t-1} dies) then 2*KSTEPS
+          // QK MFMAs (S_t is born), LDS reads kLookahead MFMAs ahead
+          const uint16_t* Kb = Ks + slot(t) * KTILE;
+          const uint16_t* Vb = Vs + slot(t - 1) * VTILE;
+          stage_pv(Vb, 0, P0);
+          stage_pv(Vb, 1, P1);
+          stage_qk(Kb, 0, S0);
+          stage_qk(Kb, 1, S1);
+          MStepSchedule<4 * DTILES, 2 * KSTEPS, kLookahead>::apply();
+        } else if (KIND == 0) {
+          // M(t): PV of tile t-1, QK of tile t, each when needed by this wave
+          if (sidx >= 0 && needed(t - 1)) {
+            const uint16_t* Vb = Vs + slot(t - 1) * VTILE;
+            stage_pv(Vb, 0, P0);
+            stage_pv(Vb, 1, P1);
+            MStepSchedule<4 * DTILES, 0, kLookahead>::apply();
           }
-        }
-        // ---- online softmax -------------------------------------------------
-        float mx = fmaxf(s0[0], s1[0]);
+          if (sidx >= 0 && needed(t)) {
+            const uint16_t* Kb = Ks + slot(t) * KTILE;
+            stage_qk(Kb, 0, S0);
+            stage_qk(Kb, 1, S1);
+            MStepSchedule<0, 2 * KSTEPS, kLookahead>::apply();
+          }
+        } else if (ALL || (sidx >= 0 && needed(t))) {
+          // V(t): mask and softmax of the 64 keys of tile t
+          if (!ALL && t * BN + BN > free_keys) {
+            // register r of S0 (S1) holds key t*BN + 4*lh + off(r) (+32): keep
+            // keys <= lim = min(row + Sk - Sq, Sk - 1) of this lane's row
+            int lim = p.Sk - 1;
+            if (CAUSAL) lim = min(lim, row + p.kv_off);
+            lim -= t * BN + 4 * lh;
 #pragma unroll
-        for (int r = 1; r < 16; ++r) mx = fmaxf(mx, fmaxf(s0[r], s1[r]));
-        mx = pair_max(mx) * c;  // this tile's row max, log2 domain
-        if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleTau)) {
-          const float m_new = fmaxf(m_run, mx);
-          const float alpha = fast_exp2(m_run - ((m_new == -__builtin_inff()) ? 0.f : m_new));
-          l_run *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < DTILES; ++dt) oacc[dt] *= alpha;
-          m_run = m_new;
-        }
-        const float m_use = (m_run == -__builtin_inff()) ? 0.f : m_run;
-        float psum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          s0[r] = fast_exp2(__builtin_fmaf(s0[r], c, -m_use));
-          s1[r] = fast_exp2(__builtin_fmaf(s1[r], c, -m_use));
-          psum += s0[r] + s1[r];
-        }
-        l_run += psum;
-        // ---- O^T += V^T P^T ---------------------------------------------------
-        if (FA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-        for (int st = 0; st < 2; ++st) {
-          const f32x16& sp = st ? s1 : s0;
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const int r0 = 8 * kk;
-            const u32x4 pb = {E::pack2(sp[r0 + 0], sp[r0 + 1]), E::pack2(sp[r0 + 2], sp[r0 + 3]),
-                              E::pack2(sp[r0 + 4], sp[r0 + 5]), E::pack2(sp[r0 + 6], sp[r0 + 7])};
-            const uint16_t* vrow = Vb + v_lane + (32 * st + 16 * kk) * VST;
-#pragma unroll
-            for (int dt = 0; dt < DTILES; ++dt) {
-              const u32x2 lo = lds_read_tr16(vrow + 32 * dt);
-              const u32x2 hi = lds_read_tr16(vrow + 8 * VST + 32 * dt);
-              const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
-              oacc[dt] = E::mfma(a, pb, oacc[dt]);
+            for (int r = 0; r < 16; ++r) {
+              const int off = 8 * (r >> 2) + (r & 3);
+              S0[r] = off > lim ? -__builtin_inff() : S0[r];
+              S1[r] = off + 32 > lim ? -__builtin_inff() : S1[r];
             }
           }
+          stage_max2(S0, S1);
+          stage_exp(S0, P0);
+          stage_exp(S1, P1);
         }
-        if (FA_MFMA_SETPRIO) __builtin_amdgcn_s_setprio(0);
+        if (do_load) {
+          if (LAG == 0) lstore_half(Ks + slot(Xld) * KTILE, KST, R);
+          else lstore_half(Vs + slot(Xld) * VTILE, VST, R);
+        }
+        // each phase is its own scheduling region: nothing drifts across the
+        // barrier that separates the two waves' roles
+        __builtin_amdgcn_sched_barrier(0);
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // phase g runs step g - LAG: an M step when it is even, a V step when odd
+      using K0 = std::integral_constant<int, LAG>;      // kind of even phases
+      using K1 = std::integral_constant<int, 1 - LAG>;  // kind of odd phases
+      int g = 0;
+      for (; g + 1 < min(4, nphase); g += 2) {
+        phase(g, K0{}, std::false_type{});
+        phase(g + 1, K1{}, std::false_type{});
       }
-
-      if (t + 1 < ntiles) lstore_tile(buf ^ 1);
-      __syncthreads();
-    }
+      for (; g + 1 < main_end; g += 2) {
+        phase(g, K0{}, std::true_type{});
+        phase(g + 1, K1{}, std::true_type{});
+      }
+      for (; g + 1 < nphase; g += 2) {
+        phase(g, K0{}, std::false_type{});
+        phase(g + 1, K1{}, std::false_type{});
+      }
+    };
+    if (wave < kPrefillWaves / 2) run(std::integral_constant<int, 0>{});
+    else run(std::integral_constant<int, 1>{});
+    (void)free_tiles;
 
     // ---- epilogue: O = O^T / l, rows < Sq --------------------------------------
     const float l_tot = pair_sum(l_run);
