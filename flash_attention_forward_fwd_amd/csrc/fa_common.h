@@ -47,6 +47,11 @@ struct Elt<kBF16> {
   static __device__ __forceinline__ float widen(unsigned short bits) {
     return __uint_as_float(((unsigned)bits) << 16);
   }
+  // acc + lo + hi of a packed pair, fp32 accumulate (v_dot2_f32_bf16 with ones)
+  static __device__ __forceinline__ float sum2(unsigned pair, float acc) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                           __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
+  }
 };
 
 template <>
@@ -64,6 +69,10 @@ struct Elt<kFP16> {
   static __device__ __forceinline__ float widen(unsigned short bits) {
     return (float)__builtin_bit_cast(_Float16, bits);
   }
+  static __device__ __forceinline__ float sum2(unsigned pair, float acc) {
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pair),
+                                  __builtin_bit_cast(f16x2, 0x3C003C00u), acc, false);
+  }
 };
 
 // 16-byte global load / store (global_load_dwordx4 / global_store_dwordx4).
@@ -77,6 +86,10 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds) {
       (__attribute__((address_space(3))) i16x4*)(lds));
   return __builtin_bit_cast(u32x2, t);
 }
+
+// s_waitcnt vmcnt(0): every vector-memory operation of this wave has finished
+// (for a buffer load to LDS: its data is in LDS)
+__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ u32x4 lds_read16(const uint16_t* lds) {
   return *reinterpret_cast<const u32x4*>(lds);

@@ -45,6 +45,12 @@ namespace {
 constexpr int kBufferFlags = 0x00020000;
 constexpr int kKPad = 8;   // K LDS row = D + 8 elements (16-byte skew per row)
 constexpr int kVPad = 32;  // V LDS row = D + 32 elements (64-byte skew per row)
+// a byte offset past the end of any K/V buffer (their byte sizes are < 2^31):
+// buffer loads from it read zeros
+constexpr unsigned kPastEnd = 0x7FFFFFF0u;
+// 1 KiB LDS-image pieces per wave per tile copy: the K image of a 64-key tile
+// has 64 (D + 8) / 512 pieces, the V image 64 (D + 32) / 512; 4 waves share them
+constexpr int kDmaSlots = 5;
 
 // The exp2 reference max of a row moves only when the row's running max
 // exceeds it by more than kRescaleTau (log2 units), so p = exp2(s*c - m_ref)
@@ -65,28 +71,34 @@ constexpr int kLookahead = FA_LOOKAHEAD;
 #define FA_MFMA_SETPRIO 0
 #endif
 
-// Instruction order of a steady-state M step for the scheduler: NPV PV MFMAs
-// (each consumes two transposing V reads) then NQK QK MFMAs (each consumes
-// one 16-byte K read).  Every read is issued LA MFMAs before its consumer.
-template <int NPV, int NQK, int LA>
-struct MStepSchedule {
-  static constexpr int NM = NPV + NQK;
-  static constexpr int reads_upto(int m) { return m <= NPV ? 2 * m : 2 * NPV + (m - NPV); }
-  template <int I>
-  static __device__ __forceinline__ void emit() {
-    if constexpr (I < NM) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-      constexpr int hi = (I + LA < NM) ? reads_upto(I + LA + 1) : reads_upto(NM);
-      constexpr int lo = (I + LA - 1 < NM) ? reads_upto(I + LA) : reads_upto(NM);
-      if constexpr (hi - lo > 0) __builtin_amdgcn_sched_group_barrier(0x100, hi - lo, 0);
-      emit<I + 1>();
-    }
+// An M step as an explicit software pipeline over its N MFMAs: the LDS
+// operand of MFMA j is read LA MFMAs before it, and a scheduling fence after
+// every (MFMA j, read j + LA) pair keeps that distance from being collapsed
+// by the compiler's own scheduling.  load(j) returns MFMA j's operand,
+// mfma(j, a) issues MFMA j.
+template <int J, int N, int LA, class Load, class Mfma>
+__device__ __forceinline__ void m_pipe(Load& load, Mfma& mfma, u32x4 (&buf)[LA]) {
+  if constexpr (J < N) {
+    mfma(std::integral_constant<int, J>{}, buf[J % LA]);
+    if constexpr (J + LA < N) buf[J % LA] = load(std::integral_constant<int, J + LA>{});
+    __builtin_amdgcn_sched_barrier(0);
+    m_pipe<J + 1, N, LA>(load, mfma, buf);
   }
-  static __device__ __forceinline__ void apply() {
-    __builtin_amdgcn_sched_group_barrier(0x100, reads_upto(LA < NM ? LA : NM), 0);  // primer
-    emit<0>();
+}
+template <int J, int N, int LA, class Load>
+__device__ __forceinline__ void m_prime(Load& load, u32x4 (&buf)[LA]) {
+  if constexpr (J < N && J < LA) {
+    buf[J] = load(std::integral_constant<int, J>{});
+    m_prime<J + 1, N, LA>(load, buf);
   }
-};
+}
+template <int N, int LA, class Load, class Mfma>
+__device__ __forceinline__ void m_pipeline(Load& load, Mfma& mfma) {
+  u32x4 buf[LA];
+  m_prime<0, N, LA>(load, buf);
+  __builtin_amdgcn_sched_barrier(0);
+  m_pipe<0, N, LA>(load, mfma, buf);
+}
 
 // Work item -> (batch, query head, query block).  Query blocks are visited
 // heaviest first (a causal block's cost grows with its index).
@@ -129,8 +141,6 @@ void prefill_kernel(PrefillParams p) {
   constexpr int KSTEPS = D / 16;     // k-steps of the QK product
   constexpr int DTILES = D / 32;     // 32-wide column tiles of O
   constexpr int CH = D / 8;          // 16-byte chunks per K/V row
-  constexpr int PER = BN * CH / NT;  // chunks per thread per tile
-  static_assert(BN * CH % NT == 0, "tile copy must divide evenly");
   static_assert(BN == 64, "a tile is two 32-key sub-tiles");
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF * KTILE];
@@ -208,44 +218,37 @@ void prefill_kernel(PrefillParams p) {
     float m_run = -__builtin_inff();  // exp2 reference max (log2 domain)
     float l_run = 0.f;                // this lane's half of the row sum
 
-    // one group (4 waves, 256 threads) copies the K or the V half of a tile
-    // global -> registers -> LDS inside its V phase; keys >= Sk become zeros
-    constexpr int GT = NT / 2;              // threads per group
-    constexpr int GPER = BN * CH / GT;      // 16-byte chunks per thread per half tile
-    static_assert(BN * CH % GT == 0, "half-tile copy must divide evenly");
-    const int gtid = tid % GT;
-    // buffer descriptors over this (batch, kv head)'s K and V: the tile offset
-    // is a scalar, the lane offset a 32-bit VGPR, and reads past Sk return 0
+    // One group (4 waves) copies the K or the V half of each tile, straight
+    // from global memory into LDS (16-byte buffer loads to LDS: lane j of a
+    // load writes bytes [16 j, 16 j + 16) after the load's LDS base), so the
+    // copy holds no registers and issues no LDS stores.  A tile's LDS image,
+    // padding included, is cut into 1 KiB pieces, one per load; image chunk
+    // c is row c / RC, column c % RC, and padding columns (>= CH) load from
+    // an offset past the buffer, which reads zeros.  Buffer descriptors span
+    // this (batch, kv head)'s K and V, so rows >= Sk read zeros too.
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(kg + kvbase), (short)0, p.Sk * D * 2, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(vg + kvbase), (short)0, p.Sk * D * 2, kBufferFlags);
-    auto gload_half = [&](__amdgpu_buffer_rsrc_t rs, int t, u32x4 (&R)[GPER]) {
-#pragma unroll
-      for (int u = 0; u < GPER; ++u) {
-        const int cidx = gtid + u * GT;
-        const int rr = cidx / CH, cc = cidx % CH;
-        R[u] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (rr * D + cc * 8) * 2, t * BN * D * 2, 0));
-      }
+    const int gw = wave % (kPrefillWaves / 2);  // wave index inside its group
+    // lane's global byte offset for load u of this wave (loads gw, gw+4, ...)
+    auto dma_offset = [&](int rc, int u) -> unsigned {
+      const int cidx = 64 * (gw + 4 * u) + lane;
+      const int rr = cidx / rc, cc = cidx - rr * rc;
+      return cc < CH ? (unsigned)((rr * D + cc * 8) * 2) : kPastEnd;
     };
-    auto lstore_half = [&](uint16_t* dst, int stride, const u32x4 (&R)[GPER]) {
+    auto dma_tile = [&](__amdgpu_buffer_rsrc_t rs, uint16_t* dst, int t, int ni,
+                        const unsigned* offs) {
 #pragma unroll
-      for (int u = 0; u < GPER; ++u) {
-        const int cidx = gtid + u * GT;
-        const int rr = cidx / CH, cc = cidx % CH;
-        lds_write16(dst + rr * stride + cc * 8, R[u]);
+      for (int u = 0; u < kDmaSlots; ++u) {
+        if (gw + 4 * u < ni)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              rs, (__attribute__((address_space(3))) void*)(dst + (gw + 4 * u) * 512), 16,
+              offs[u], t * BN * D * 2, 0, 0);
       }
     };
 
     // ---- the three stages of a 32-key sub-tile ---------------------------------
-    // A: S^T = K Q^T for keys [32 st, 32 st + 32) of the tile in buffer Kb
-    auto stage_qk = [&](const uint16_t* Kb, int st, f32x16& S) {
-      S = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk)
-        S = E::mfma(lds_read16(Kb + k_lane + 32 * st * KST + 16 * kk), qr[kk], S);
-    };
     // B1: row max of the sub-tile (log2 domain); move the reference max and
     // rescale O and l when some row of the wave jumped above it by > tau
     auto stage_max = [&](const f32x16& S) {
@@ -296,18 +299,40 @@ void prefill_kernel(PrefillParams p) {
                       E::pack2(S[r0 + 4], S[r0 + 5]), E::pack2(S[r0 + 6], S[r0 + 7])};
       }
     };
-    // C: O^T += V^T P^T for keys [32 st, 32 st + 32) of the tile in buffer Vb
-    auto stage_pv = [&](const uint16_t* Vb, int st, const u32x4 (&P)[2]) {
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const uint16_t* vrow = Vb + v_lane + (32 * st + 16 * kk) * VST;
-#pragma unroll
-        for (int dt = 0; dt < DTILES; ++dt) {
-          const u32x2 lo = lds_read_tr16(vrow + 32 * dt);
-          const u32x2 hi = lds_read_tr16(vrow + 8 * VST + 32 * dt);
-          oacc[dt] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, P[kk], oacc[dt]);
+    // M step: NPV PV MFMAs then NQK QK MFMAs.
+    //   PV (C): O^T += V^T P^T for tile Vb; MFMA j = (sub-tile st, k-step kk,
+    //     column tile dt) reads its V^T operand with two transposing reads
+    //     of the row-major V tile
+    //   QK (A): S^T = K Q^T for tile Kb; MFMA j = (sub-tile st, k-step kk)
+    //     reads one 16-byte K row chunk
+    auto m_step = [&](auto npv_c, auto nqk_c, const uint16_t* Vb, const uint16_t* Kb,
+                      const u32x4 (&P0)[2], const u32x4 (&P1)[2], f32x16& S0, f32x16& S1) {
+      constexpr int NPV = decltype(npv_c)::value, NQK = decltype(nqk_c)::value;
+      auto load = [&](auto jc) -> u32x4 {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (j < NPV) {
+          constexpr int st = j / (2 * DTILES), kk = (j / DTILES) % 2, dt = j % DTILES;
+          const uint16_t* vrow = Vb + v_lane + (32 * st + 16 * kk) * VST + 32 * dt;
+          const u32x2 lo = lds_read_tr16(vrow);
+          const u32x2 hi = lds_read_tr16(vrow + 8 * VST);
+          return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          constexpr int q = j - NPV, st = q / KSTEPS, kk = q % KSTEPS;
+          return lds_read16(Kb + k_lane + 32 * st * KST + 16 * kk);
         }
-      }
+      };
+      auto mfma = [&](auto jc, u32x4 a) {
+        constexpr int j = decltype(jc)::value;
+        if constexpr (j < NPV) {
+          constexpr int st = j / (2 * DTILES), kk = (j / DTILES) % 2, dt = j % DTILES;
+          oacc[dt] = E::mfma(a, st == 0 ? P0[kk] : P1[kk], oacc[dt]);
+        } else {
+          constexpr int q = j - NPV, st = q / KSTEPS, kk = q % KSTEPS;
+          f32x16& S = st == 0 ? S0 : S1;
+          S = E::mfma(a, qr[kk], kk == 0 ? f32x16{} : S);
+        }
+      };
+      m_pipeline<NPV + NQK, kLookahead>(load, mfma);
     };
 
     // ---- ping-pong schedule ----------------------------------------------------
@@ -335,20 +360,26 @@ void prefill_kernel(PrefillParams p) {
     // every wave and mask-free
     const int main_end = 2 * main_tiles - 2;
 
+    constexpr int KRC = KST / 8, VRC = VST / 8;        // 16-byte chunks per LDS row
+    constexpr int KNI = BN * KRC / 64, VNI = BN * VRC / 64;  // 1 KiB pieces per tile
+    static_assert(BN * KRC % 64 == 0 && BN * VRC % 64 == 0, "tile images are whole KiB");
+    static_assert(KNI <= 4 * kDmaSlots && VNI <= 4 * kDmaSlots, "copy slots per wave");
+    const bool lead = wave < kPrefillWaves / 2;
+    // this wave's per-lane source offsets: K pieces for the leading group,
+    // V pieces for the following one
+    unsigned dma_offs[kDmaSlots];
+#pragma unroll
+    for (int u = 0; u < kDmaSlots; ++u) dma_offs[u] = dma_offset(lead ? KRC : VRC, u);
+
     // prologue: the leading group copies K of tiles 0 and 1, the following V
-    {
-      const bool lead = wave < kPrefillWaves / 2;
-      u32x4 R0[GPER], R1[GPER];
-      gload_half(lead ? krs : vrs, 0, R0);
-      if (ntiles > 1) gload_half(lead ? krs : vrs, 1, R1);
-      if (lead) {
-        lstore_half(Ks, KST, R0);
-        if (ntiles > 1) lstore_half(Ks + slot(1) * KTILE, KST, R1);
-      } else {
-        lstore_half(Vs, VST, R0);
-        if (ntiles > 1) lstore_half(Vs + slot(1) * VTILE, VST, R1);
-      }
+    if (lead) {
+      dma_tile(krs, Ks, 0, KNI, dma_offs);
+      if (ntiles > 1) dma_tile(krs, Ks + slot(1) * KTILE, 1, KNI, dma_offs);
+    } else {
+      dma_tile(vrs, Vs, 0, VNI, dma_offs);
+      if (ntiles > 1) dma_tile(vrs, Vs + slot(1) * VTILE, 1, VNI, dma_offs);
     }
+    wait_loads();
     __syncthreads();
 
     auto run = [&](auto lag_c) {
@@ -365,8 +396,10 @@ void prefill_kernel(PrefillParams p) {
         // group V(X) in its V phase 2X-2 (tiles 0 and 1 come with the prologue)
         const int Xld = LAG == 0 ? (g + 3) >> 1 : (g + 2) >> 1;
         const bool do_load = KIND == 1 && Xld >= 2 && Xld < ntiles;
-        u32x4 R[GPER];
-        if (do_load) gload_half(LAG == 0 ? krs : vrs, Xld, R);
+        if (do_load) {
+          if (LAG == 0) dma_tile(krs, Ks + slot(Xld) * KTILE, Xld, KNI, dma_offs);
+          else dma_tile(vrs, Vs + slot(Xld) * VTILE, Xld, VNI, dma_offs);
+        }
         const int sidx = g - LAG;
         const int t = sidx >> 1;
         if (KIND == 0 && ALL) {
@@ -374,24 +407,19 @@ void prefill_kernel(PrefillParams p) {
           // QK MFMAs (S_t is born), LDS reads kLookahead MFMAs ahead
           const uint16_t* Kb = Ks + slot(t) * KTILE;
           const uint16_t* Vb = Vs + slot(t - 1) * VTILE;
-          stage_pv(Vb, 0, P0);
-          stage_pv(Vb, 1, P1);
-          stage_qk(Kb, 0, S0);
-          stage_qk(Kb, 1, S1);
-          MStepSchedule<4 * DTILES, 2 * KSTEPS, kLookahead>::apply();
+          m_step(std::integral_constant<int, 4 * DTILES>{}, std::integral_constant<int, 2 * KSTEPS>{},
+                 Vb, Kb, P0, P1, S0, S1);
         } else if (KIND == 0) {
           // M(t): PV of tile t-1, QK of tile t, each when needed by this wave
           if (sidx >= 0 && needed(t - 1)) {
             const uint16_t* Vb = Vs + slot(t - 1) * VTILE;
-            stage_pv(Vb, 0, P0);
-            stage_pv(Vb, 1, P1);
-            MStepSchedule<4 * DTILES, 0, kLookahead>::apply();
+            m_step(std::integral_constant<int, 4 * DTILES>{}, std::integral_constant<int, 0>{},
+                   Vb, Ks, P0, P1, S0, S1);
           }
           if (sidx >= 0 && needed(t)) {
             const uint16_t* Kb = Ks + slot(t) * KTILE;
-            stage_qk(Kb, 0, S0);
-            stage_qk(Kb, 1, S1);
-            MStepSchedule<0, 2 * KSTEPS, kLookahead>::apply();
+            m_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 2 * KSTEPS>{},
+                   Vs, Kb, P0, P1, S0, S1);
           }
         } else if (ALL || (sidx >= 0 && needed(t))) {
           // V(t): mask and softmax of the 64 keys of tile t
@@ -412,13 +440,11 @@ void prefill_kernel(PrefillParams p) {
           stage_exp(S0, P0);
           stage_exp(S1, P1);
         }
-        if (do_load) {
-          if (LAG == 0) lstore_half(Ks + slot(Xld) * KTILE, KST, R);
-          else lstore_half(Vs + slot(Xld) * VTILE, VST, R);
-        }
         // each phase is its own scheduling region: nothing drifts across the
-        // barrier that separates the two waves' roles
+        // barrier that separates the two waves' roles; the tile copied in
+        // this phase has landed in LDS before the barrier
         __builtin_amdgcn_sched_barrier(0);
+        if (do_load) wait_loads();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
       };
