@@ -67,9 +67,12 @@ constexpr float kRescaleTau = FA_RESCALE_TAU;
 #define FA_LOOKAHEAD 4
 #endif
 constexpr int kLookahead = FA_LOOKAHEAD;
+// wave priority of the MFMA step (s_setprio; 0 = default) while the other
+// wave of its SIMD runs the vector step
 #ifndef FA_MFMA_SETPRIO
 #define FA_MFMA_SETPRIO 0
 #endif
+constexpr int kMfmaPrio = FA_MFMA_SETPRIO;
 
 // An M step as an explicit software pipeline over its N MFMAs: the LDS
 // operand of MFMA j is read LA MFMAs before it, and a scheduling fence after
@@ -395,13 +398,19 @@ void prefill_kernel(PrefillParams p) {
         // the leading group copies K(X) in its V phase 2X-3, the following
         // group V(X) in its V phase 2X-2 (tiles 0 and 1 come with the prologue)
         const int Xld = LAG == 0 ? (g + 3) >> 1 : (g + 2) >> 1;
-        const bool do_load = KIND == 1 && Xld >= 2 && Xld < ntiles;
+        // in the straight-line body every V phase copies (a copy of tile
+        // ntiles reads zeros past Sk into a ring slot no one reads), so the
+        // copy and its completion wait carry no branch: a branch there lets
+        // the compiler sink the softmax below the wait and expose the load
+        // latency
+        const bool do_load = KIND == 1 && (ALL || (Xld >= 2 && Xld < ntiles));
         if (do_load) {
           if (LAG == 0) dma_tile(krs, Ks + slot(Xld) * KTILE, Xld, KNI, dma_offs);
           else dma_tile(vrs, Vs + slot(Xld) * VTILE, Xld, VNI, dma_offs);
         }
         const int sidx = g - LAG;
         const int t = sidx >> 1;
+        if constexpr (KIND == 0 && kMfmaPrio > 0) __builtin_amdgcn_s_setprio(kMfmaPrio);
         if (KIND == 0 && ALL) {
           // M(t), steady state: 4*DTILES PV MFMAs (P_{t-1} dies) then 2*KSTEPS
           // QK MFMAs (S_t is born), LDS reads kLookahead MFMAs ahead
@@ -440,6 +449,7 @@ void prefill_kernel(PrefillParams p) {
           stage_exp(S0, P0);
           stage_exp(S1, P1);
         }
+        if constexpr (KIND == 0 && kMfmaPrio > 0) __builtin_amdgcn_s_setprio(0);
         // each phase is its own scheduling region: nothing drifts across the
         // barrier that separates the two waves' roles; the tile copied in
         // this phase has landed in LDS before the barrier
