@@ -19,6 +19,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -87,9 +88,12 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds) {
   return __builtin_bit_cast(u32x2, t);
 }
 
+// gfx9 buffer resource word 3: 32-bit data format, raw (unswizzled) access
+constexpr int kBufferFlags = 0x00020000;
+
 // s_waitcnt vmcnt(0): every vector-memory operation of this wave has finished
 // (for a buffer load to LDS: its data is in LDS)
-__device__ __forceinline__ void wait_loads() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 __device__ __forceinline__ u32x4 lds_read16(const uint16_t* lds) {
   return *reinterpret_cast<const u32x4*>(lds);

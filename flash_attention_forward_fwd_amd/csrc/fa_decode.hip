@@ -38,68 +38,141 @@ constexpr int kDVPad = 32;       // V staging row pad (elements)
 __device__ __forceinline__ int heads_in_group(int gqa, int hg) { return min(32, gqa - 32 * hg); }
 
 // Partials cross workgroups (and XCDs, whose L2 caches are not coherent with
-// each other) through agent-scope relaxed atomic loads and stores: they are
-// written through to the device-coherent level and read from it, so no
-// whole-cache writeback or invalidate (what a device-scope fence costs on
-// gfx950) is needed.  Ordering comes from waiting for the stores to complete
-// (vmcnt(0)) before the ticket is taken.
-__device__ __forceinline__ float ld_coherent(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// each other) through loads and stores with the sc1 cache policy (what an
+// agent-scope relaxed atomic access compiles to): they are written through to
+// the device-coherent level and read from it, so no whole-cache writeback or
+// invalidate (what a device-scope fence costs on gfx950) is needed.  Ordering
+// comes from waiting for the stores to complete (vmcnt(0)) before the ticket
+// is taken.
+// Coherent 16- and 8-byte accesses to one unit's partial records.
+constexpr int kCoherent = 16;  // cache-policy bits: sc1
+__device__ __forceinline__ f32x4 ld4_coherent(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCoherent));
 }
-__device__ __forceinline__ void st_coherent(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+__device__ __forceinline__ void st4_coherent(__amdgpu_buffer_rsrc_t rs, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, kCoherent);
 }
-__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }  // vmcnt(0)
+__device__ __forceinline__ f32x2 ld2_coherent(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kCoherent));
+}
+__device__ __forceinline__ void st2_coherent(__amdgpu_buffer_rsrc_t rs, int off, f32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, off, 0, kCoherent);
+}
 
-// Merge `n` partial records [first, first + n) of (src_o, src_ml) -- LDS when
-// SRC_LDS, otherwise global -- into one unnormalised record (dst_o, dst_ml) in
-// global memory, or, when `out` is not null, normalise and write O.
-template <int D, int DT, bool SRC_LDS>
-__device__ void merge_partials(const float* src_o, const float* src_ml, int first, int n, int gg,
-                               float* dst_o, float* dst_ml, uint16_t* out, long long out_base,
-                               float* lds_scratch) {
+// Merge records [first, first + n) (n <= kMergeGroup) of one unit's partials
+// in global memory -- o records of gg x D floats at byte 0 of `ro`, (m, l)
+// pairs at byte 0 of `rml` -- into record `dst` of the same unit, or, when
+// `out` is not null, normalise and write O.  Every thread issues all of its
+// record loads before using any, so a merge costs about one memory round trip.
+template <int D, int DT>
+__device__ void merge_global(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rml, int first,
+                             int n, int gg, int dst, uint16_t* out, long long out_base,
+                             float* lds_scratch) {
   using E = Elt<DT>;
-  auto ld = [](const float* p) { return SRC_LDS ? *p : ld_coherent(p); };
-  float* w = lds_scratch;              // [gg][n] weights 2^(m_s - M)
-  float* den = lds_scratch + gg * n;   // [gg]
-  float* Mh = den + gg;                // [gg]
+  constexpr int Q = D / 4;              // 16-byte pieces per head row
+  float* w = lds_scratch;               // [gg][kMergeGroup] weights 2^(m_s - M)
+  float* den = w + gg * kMergeGroup;    // [gg]
+  float* Mh = den + gg;                 // [gg]
   for (int g = threadIdx.x; g < gg; g += blockDim.x) {
+    f32x2 ml[kMergeGroup];
+#pragma unroll
+    for (int s = 0; s < kMergeGroup; ++s)
+      if (s < n) ml[s] = ld2_coherent(rml, ((first + s) * gg + g) * 8);
     float M = -__builtin_inff();
-    for (int s = 0; s < n; ++s) M = fmaxf(M, ld(src_ml + ((long long)(first + s) * gg + g) * 2));
+#pragma unroll
+    for (int s = 0; s < kMergeGroup; ++s)
+      if (s < n) M = fmaxf(M, ml[s][0]);
     const float Mu = (M == -__builtin_inff()) ? 0.f : M;
     float dsum = 0.f;
-    for (int s = 0; s < n; ++s) {
-      const float m = ld(src_ml + ((long long)(first + s) * gg + g) * 2 + 0);
-      const float l = ld(src_ml + ((long long)(first + s) * gg + g) * 2 + 1);
-      const float f = fast_exp2(m - Mu);  // m = -inf -> 0
-      w[g * n + s] = f;
-      dsum += f * l;
+#pragma unroll
+    for (int s = 0; s < kMergeGroup; ++s) {
+      if (s < n) {
+        const float f = fast_exp2(ml[s][0] - Mu);  // m = -inf -> 0
+        w[g * kMergeGroup + s] = f;
+        dsum += f * ml[s][1];
+      }
     }
     den[g] = dsum;
     Mh[g] = M;
   }
   __syncthreads();
-  for (int idx = threadIdx.x; idx < gg * D; idx += blockDim.x) {
-    const int g = idx / D, d = idx - g * D;
-    float acc = 0.f;
+  for (int idx = threadIdx.x; idx < gg * Q; idx += blockDim.x) {
+    const int g = idx / Q, q = idx - g * Q;
+    f32x4 x[kMergeGroup];
+#pragma unroll
+    for (int s = 0; s < kMergeGroup; ++s)
+      if (s < n) x[s] = ld4_coherent(ro, (((first + s) * gg + g) * D + 4 * q) * 4);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < kMergeGroup; ++s) {
+      if (s < n) {
+        const float f = w[g * kMergeGroup + s];
+        if (f != 0.f) acc += f * x[s];
+      }
+    }
+    if (out) {
+      const float dd = den[g];
+      const float inv = dd > 0.f ? 1.0f / dd : 0.f;
+      const u32x2 pk = {E::pack2(acc[0] * inv, acc[1] * inv), E::pack2(acc[2] * inv, acc[3] * inv)};
+      *reinterpret_cast<u32x2*>(out + out_base + (long long)g * D + 4 * q) = pk;
+    } else {
+      st4_coherent(ro, ((dst * gg + g) * D + 4 * q) * 4, acc);
+    }
+  }
+  if (!out) {
+    for (int g = threadIdx.x; g < gg; g += blockDim.x)
+      st2_coherent(rml, (dst * gg + g) * 8, f32x2{Mh[g], den[g]});
+  }
+  __syncthreads();
+}
+
+// Merge the workgroup's `n` wave records (o: [n][gg][D], ml: [n][gg][2], in
+// LDS) into record `dst` of the unit's partials in global memory (written
+// coherently, 16 bytes at a time), or, when `out` is not null, normalise and
+// write O.
+template <int D, int DT>
+__device__ void merge_waves(const float* src_o, const float* src_ml, int n, int gg,
+                            __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rml, int dst,
+                            uint16_t* out, long long out_base, float* lds_scratch) {
+  using E = Elt<DT>;
+  constexpr int Q = D / 4;
+  float* w = lds_scratch;              // [gg][n] weights 2^(m_s - M)
+  float* den = lds_scratch + gg * n;   // [gg]
+  float* Mh = den + gg;                // [gg]
+  for (int g = threadIdx.x; g < gg; g += blockDim.x) {
+    float M = -__builtin_inff();
+    for (int s = 0; s < n; ++s) M = fmaxf(M, src_ml[(s * gg + g) * 2]);
+    const float Mu = (M == -__builtin_inff()) ? 0.f : M;
+    float dsum = 0.f;
+    for (int s = 0; s < n; ++s) {
+      const float f = fast_exp2(src_ml[(s * gg + g) * 2] - Mu);  // m = -inf -> 0
+      w[g * n + s] = f;
+      dsum += f * src_ml[(s * gg + g) * 2 + 1];
+    }
+    den[g] = dsum;
+    Mh[g] = M;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < gg * Q; idx += blockDim.x) {
+    const int g = idx / Q, q = idx - g * Q;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < n; ++s) {
       const float f = w[g * n + s];
-      const float x = ld(src_o + ((long long)(first + s) * gg + g) * D + d);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src_o + (s * gg + g) * D + 4 * q);
       if (f != 0.f) acc += f * x;
     }
     if (out) {
       const float dd = den[g];
-      const float val = dd > 0.f ? acc / dd : 0.f;
-      out[out_base + (long long)g * D + d] = (uint16_t)(E::pack2(val, 0.f) & 0xFFFFu);
+      const float inv = dd > 0.f ? 1.0f / dd : 0.f;
+      const u32x2 pk = {E::pack2(acc[0] * inv, acc[1] * inv), E::pack2(acc[2] * inv, acc[3] * inv)};
+      *reinterpret_cast<u32x2*>(out + out_base + (long long)g * D + 4 * q) = pk;
     } else {
-      st_coherent(dst_o + (long long)g * D + d, acc);
+      st4_coherent(ro, ((dst * gg + g) * D + 4 * q) * 4, acc);
     }
   }
   if (!out) {
-    for (int g = threadIdx.x; g < gg; g += blockDim.x) {
-      st_coherent(dst_ml + g * 2 + 0, Mh[g]);
-      st_coherent(dst_ml + g * 2 + 1, den[g]);
-    }
+    for (int g = threadIdx.x; g < gg; g += blockDim.x)
+      st2_coherent(rml, (dst * gg + g) * 8, f32x2{Mh[g], den[g]});
   }
   __syncthreads();
 }
@@ -108,7 +181,7 @@ __device__ void merge_partials(const float* src_o, const float* src_ml, int firs
 // thread of the workgroup that arrives last (count reaches `total`); that
 // workgroup also resets the counter for the next call.
 __device__ __forceinline__ bool take_ticket(unsigned* counter, unsigned total, int* lds_flag) {
-  wait_stores();
+  wait_vmem();  // this workgroup's record stores have completed
   __syncthreads();
   if (threadIdx.x == 0) {
     const unsigned t =
@@ -122,7 +195,7 @@ __device__ __forceinline__ bool take_ticket(unsigned* counter, unsigned total, i
 }
 
 template <int D, int DT>
-__global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(DecodeParams p) {
+__global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_kernel(DecodeParams p) {
   using E = Elt<DT>;
   constexpr int NW = kDecodeWaves;
   constexpr int KSTEPS = D / 16;
@@ -276,20 +349,22 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(DecodeParams 
     }
   }
   __syncthreads();
-  float* scratch = wml + NW * gg * 2;  // [gg][NW] weights + [gg] + [gg]
+  float* scratch = wml + NW * gg * 2;  // merge weights and per-head sums
   const int ngroups = (p.nsplit + kMergeGroup - 1) / kMergeGroup;
-  const long long unit_parts = (long long)unit * (p.nsplit + ngroups);
-  float* part_o = p.part_o + unit_parts * gg * D;   // level 0 then level 1 records
-  float* part_ml = p.part_ml + unit_parts * gg * 2;
+  const int nrec = p.nsplit + ngroups;  // level-0 records, then level-1 records
+  const long long unit_parts = (long long)unit * nrec;
+  const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
+      p.part_o + unit_parts * gg * D, (short)0, nrec * gg * D * 4, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t rml = __builtin_amdgcn_make_buffer_rsrc(
+      p.part_ml + unit_parts * gg * 2, (short)0, nrec * gg * 2 * 4, kBufferFlags);
   uint16_t* og = static_cast<uint16_t*>(p.o);
   const long long out_base = ((long long)b * p.Hq + hq0) * D;
 
   if (p.nsplit == 1) {
-    merge_partials<D, DT, true>(wo, wml, 0, NW, gg, nullptr, nullptr, og, out_base, scratch);
+    merge_waves<D, DT>(wo, wml, NW, gg, ro, rml, 0, og, out_base, scratch);
     return;
   }
-  merge_partials<D, DT, true>(wo, wml, 0, NW, gg, part_o + (long long)split * gg * D,
-                        part_ml + (long long)split * gg * 2, nullptr, 0, scratch);
+  merge_waves<D, DT>(wo, wml, NW, gg, ro, rml, split, nullptr, 0, scratch);
 
   // ---- level 1: last workgroup of the group merges the group -------------------
   const int grp = split / kMergeGroup;
@@ -298,17 +373,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) void decode_kernel(DecodeParams 
   unsigned* cnt0 = p.tickets + (long long)unit * (ngroups + 1);
   if (!take_ticket(cnt0 + grp, (unsigned)gsize, &ticket_flag)) return;
   if (ngroups == 1) {
-    merge_partials<D, DT, false>(part_o, part_ml, gfirst, gsize, gg, nullptr, nullptr, og, out_base,
-                          scratch);
+    merge_global<D, DT>(ro, rml, gfirst, gsize, gg, 0, og, out_base, scratch);
     return;
   }
-  merge_partials<D, DT, false>(part_o, part_ml, gfirst, gsize, gg,
-                        part_o + (long long)(p.nsplit + grp) * gg * D,
-                        part_ml + (long long)(p.nsplit + grp) * gg * 2, nullptr, 0, scratch);
+  merge_global<D, DT>(ro, rml, gfirst, gsize, gg, p.nsplit + grp, nullptr, 0, scratch);
   // ---- level 2: last group merger merges the groups and writes O -----------
   if (!take_ticket(cnt0 + ngroups, (unsigned)ngroups, &ticket_flag)) return;
-  merge_partials<D, DT, false>(part_o, part_ml, p.nsplit, ngroups, gg, nullptr, nullptr, og, out_base,
-                        scratch);
+  merge_global<D, DT>(ro, rml, p.nsplit, ngroups, gg, 0, og, out_base, scratch);
 }
 
 template <int D, int DT>

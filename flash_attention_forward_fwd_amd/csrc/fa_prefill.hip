@@ -41,8 +41,6 @@
 namespace fa {
 namespace {
 
-// gfx9 buffer resource word 3: 32-bit data format, raw (unswizzled) access
-constexpr int kBufferFlags = 0x00020000;
 constexpr int kKPad = 8;   // K LDS row = D + 8 elements (16-byte skew per row)
 constexpr int kVPad = 32;  // V LDS row = D + 32 elements (64-byte skew per row)
 // a byte offset past the end of any K/V buffer (their byte sizes are < 2^31):
@@ -382,7 +380,7 @@ void prefill_kernel(PrefillParams p) {
       dma_tile(vrs, Vs, 0, VNI, dma_offs);
       if (ntiles > 1) dma_tile(vrs, Vs + slot(1) * VTILE, 1, VNI, dma_offs);
     }
-    wait_loads();
+    wait_vmem();
     __syncthreads();
 
     auto run = [&](auto lag_c) {
@@ -454,7 +452,7 @@ void prefill_kernel(PrefillParams p) {
         // barrier that separates the two waves' roles; the tile copied in
         // this phase has landed in LDS before the barrier
         __builtin_amdgcn_sched_barrier(0);
-        if (do_load) wait_loads();
+        if (do_load) wait_vmem();
         __syncthreads();
         __builtin_amdgcn_sched_barrier(0);
       };
