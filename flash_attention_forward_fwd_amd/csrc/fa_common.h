@@ -90,10 +90,31 @@ __device__ __forceinline__ u32x2 lds_read_tr16(const uint16_t* lds) {
 
 // gfx9 buffer resource word 3: 32-bit data format, raw (unswizzled) access
 constexpr int kBufferFlags = 0x00020000;
+// a byte offset past the end of any buffer range the kernels describe (their
+// sizes are < 2^31): buffer loads from it read zeros
+constexpr unsigned kPastEnd = 0x7FFFFFF0u;
 
 // s_waitcnt vmcnt(0): every vector-memory operation of this wave has finished
 // (for a buffer load to LDS: its data is in LDS)
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+// s_waitcnt vmcnt(N): at most N vector-memory operations of this wave are
+// still outstanding (they complete in order, so all older ones are done)
+template <int N>
+__device__ __forceinline__ void wait_vmem_le() {
+  static_assert(N >= 0 && N < 64, "vmcnt is a 6-bit count");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x0F70);
+}
+
+// 16-byte buffer load straight to LDS: lane j of the wave writes bytes
+// [16 j, 16 j + 16) after `dst` (a wave-uniform LDS address) with the 16
+// bytes at byte offset voff + soff of the buffer (zeros past its end).  A
+// function of its own: used directly inside a kernel's lambdas, the builtin
+// kept the host-side launch stub of the kernel from being emitted.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t rs, uint16_t* dst, unsigned voff,
+                                          int soff) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16,
+                                           voff, soff, 0, 0);
+}
 
 __device__ __forceinline__ u32x4 lds_read16(const uint16_t* lds) {
   return *reinterpret_cast<const u32x4*>(lds);

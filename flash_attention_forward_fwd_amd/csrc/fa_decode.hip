@@ -33,6 +33,12 @@ namespace fa {
 namespace {
 
 constexpr int kMergeGroup = 16;  // partials merged by one workgroup
+// Merge the split records in a second, stream-ordered kernel (1) instead of
+// by the last workgroups of the decode kernel through tickets (0).
+#ifndef FA_DECODE_MERGE_KERNEL
+#define FA_DECODE_MERGE_KERNEL 1
+#endif
+constexpr bool kMergeKernel = FA_DECODE_MERGE_KERNEL != 0;
 constexpr int kDVPad = 32;       // V staging row pad (elements)
 
 __device__ __forceinline__ int heads_in_group(int gqa, int hg) { return min(32, gqa - 32 * hg); }
@@ -44,6 +50,29 @@ __device__ __forceinline__ int heads_in_group(int gqa, int hg) { return min(32, 
 // invalidate (what a device-scope fence costs on gfx950) is needed.  Ordering
 // comes from waiting for the stores to complete (vmcnt(0)) before the ticket
 // is taken.
+// A transposing 64-bit LDS read (see the lane mapping in the common header)
+// as inline asm, opaque to the compiler's memory-dependency tracking; the
+// caller waits for it (lgkmcnt) and then passes the value through
+// after_wait(), which orders its uses after that wait.
+// (The host pass of the compiler sees no body: the asm names GPU registers.)
+__device__ __forceinline__ u32x2 lds_read_tr16_opaque(const uint16_t* lds) {
+  u32x2 r = {0u, 0u};
+#if defined(__HIP_DEVICE_COMPILE__)
+  const unsigned a = (unsigned)(uintptr_t)(__attribute__((address_space(3))) const void*)lds;
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(r) : "v"(a));
+#else
+  (void)lds;
+#endif
+  return r;
+}
+__device__ __forceinline__ void after_wait(u32x2& x) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("" : "+v"(x));
+#else
+  (void)x;
+#endif
+}
+
 // Coherent 16- and 8-byte accesses to one unit's partial records.
 constexpr int kCoherent = 16;  // cache-policy bits: sc1
 __device__ __forceinline__ f32x4 ld4_coherent(__amdgpu_buffer_rsrc_t rs, int off) {
@@ -201,9 +230,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   constexpr int KSTEPS = D / 16;
   constexpr int DTILES = D / 32;
   constexpr int VST = D + kDVPad;
-  constexpr int VPER = 32 * (D / 8) / 64;  // 16-byte V pieces per lane per chunk
   extern __shared__ __attribute__((aligned(16))) unsigned char dyn_lds[];
-  __shared__ int ticket_flag;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -246,44 +273,52 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     qr[kk] = x;
   }
 
-  uint16_t* vst = reinterpret_cast<uint16_t*>(dyn_lds) + wave * 32 * VST;
+  // K and V of this (batch, kv head) as buffer ranges that end at token L:
+  // token j's row sits at byte j * tok_stride * 2, and rows at or past L read
+  // zeros, so the invalid tail is never fetched
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(kg + cache_base), (short)0, (int)(L * tok_stride * 2), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(vg + cache_base), (short)0, (int)(L * tok_stride * 2), kBufferFlags);
+
+  // V of a chunk goes straight into wave-private LDS (two buffers, so the next
+  // chunk lands while this one is used) with 16-byte buffer loads to LDS: the
+  // padded 32-row image is cut into 1 KiB pieces, chunk c of the image being
+  // row c / RC, column c % RC; padding columns read from past the buffer.
+  constexpr int RC = VST / 8;                 // 16-byte chunks per staged row
+  constexpr int NPC = 32 * RC / 64;           // 1 KiB pieces per chunk
+  static_assert(32 * RC % 64 == 0, "staged V chunk is whole KiB");
+  uint16_t* vst0 = reinterpret_cast<uint16_t*>(dyn_lds) + wave * 2 * 32 * VST;
+  unsigned voffs[NPC];
+#pragma unroll
+  for (int i = 0; i < NPC; ++i) {
+    const int cidx = 64 * i + lane;
+    const int rr = cidx / RC, cc = cidx - rr * RC;
+    voffs[i] = cc < D / 8 ? (unsigned)((rr * tok_stride + cc * 8) * 2) : kPastEnd;
+  }
   const int v_lane = (4 * lh + (ti >> 2)) * VST + 16 * ((lane >> 4) & 1) + 4 * (ti & 3);
+  // K rows (A operand): lane row li, d = 16kk + 8lh
+  const unsigned k_off = (unsigned)((li * tok_stride + 8 * lh) * 2);
 
   f32x16 oacc[DTILES];
 #pragma unroll
   for (int dt = 0; dt < DTILES; ++dt) oacc[dt] = f32x16{};
   float m_run = -__builtin_inff(), l_run = 0.f;
 
-  for (int ch = c0 + wave; ch < c1; ch += NW) {
+  auto load_chunk = [&](int ch, u32x4 (&kr)[KSTEPS], uint16_t* vbuf) {
+    const int soff = ch * 32 * (int)tok_stride * 2;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      kr[kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_off + 32 * kk, soff, 0));
+#pragma unroll
+    for (int i = 0; i < NPC; ++i)
+      lds_dma16(vrs, vbuf + i * 512, voffs[i], soff);
+  };
+  auto compute_chunk = [&](int ch, const u32x4 (&kr)[KSTEPS], const uint16_t* vbuf) {
     const int tok0 = ch * 32;
-    // K rows (A operand): lane row li, d = 16kk + 8lh
-    u32x4 kr[KSTEPS];
-    const int ktok = tok0 + li;
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (ktok < L) x = gload16(kg + cache_base + (long long)ktok * tok_stride + 16 * kk + 8 * lh);
-      kr[kk] = x;
-    }
-    // V rows -> wave-private LDS, invalid rows as zeros
-    u32x4 vr[VPER];
-#pragma unroll
-    for (int u = 0; u < VPER; ++u) {
-      const int piece = lane + 64 * u;
-      const int rr = piece / (D / 8), cc = piece % (D / 8);
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (tok0 + rr < L) x = gload16(vg + cache_base + (long long)(tok0 + rr) * tok_stride + cc * 8);
-      vr[u] = x;
-    }
     f32x16 s = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) s = E::mfma(kr[kk], qr[kk], s);
-#pragma unroll
-    for (int u = 0; u < VPER; ++u) {
-      const int piece = lane + 64 * u;
-      const int rr = piece / (D / 8), cc = piece % (D / 8);
-      lds_write16(vst + rr * VST + cc * 8, vr[u]);
-    }
     // scores of tokens >= L are excluded (their K rows were zero, not -inf)
     if (tok0 + 32 > L) {
 #pragma unroll
@@ -309,25 +344,68 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     m_run = m_new;
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt) oacc[dt] *= alpha;
-    // LDS writes above must land before the transposing reads: one wave,
-    // in-order LDS queue, but make the dependency explicit
+    // V^T operands by transposing LDS reads, all issued before any is used.
+    // They are written as inline asm: the compiler cannot tell which LDS
+    // bytes a buffer load to LDS fills, and for its own reads it would wait
+    // for every such load in flight -- including the next chunk's, which is
+    // what must stay in flight here.  This chunk's pieces landed at the
+    // vmcnt wait before the call, and the lgkmcnt wait below is the reads' own.
+    u32x2 tr[2][DTILES][2];
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          tr[kk][dt][h] = lds_read_tr16_opaque(vbuf + v_lane + 16 * kk * VST + 8 * h * VST + 32 * dt);
     __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) after_wait(tr[kk][dt][h]);
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       const int r0 = 8 * kk;
       const u32x4 pb = {E::pack2(s[r0 + 0], s[r0 + 1]), E::pack2(s[r0 + 2], s[r0 + 3]),
                         E::pack2(s[r0 + 4], s[r0 + 5]), E::pack2(s[r0 + 6], s[r0 + 7])};
-      const uint16_t* vrow = vst + v_lane + 16 * kk * VST;
 #pragma unroll
       for (int dt = 0; dt < DTILES; ++dt) {
-        const u32x2 lo = lds_read_tr16(vrow + 32 * dt);
-        const u32x2 hi = lds_read_tr16(vrow + 8 * VST + 32 * dt);
-        const u32x4 a = {lo[0], lo[1], hi[0], hi[1]};
+        const u32x4 a = {tr[kk][dt][0][0], tr[kk][dt][0][1], tr[kk][dt][1][0], tr[kk][dt][1][1]};
         oacc[dt] = E::mfma(a, pb, oacc[dt]);
       }
     }
-    // the next chunk overwrites this wave's V staging: reads must be done
-    __builtin_amdgcn_s_waitcnt(0xc07f);
+  };
+
+  // chunks c0 + wave, + NW, ...: the next chunk's K and V loads are issued
+  // before the current one is computed, so two chunks are in flight per wave
+  {
+    u32x4 kA[KSTEPS], kB[KSTEPS];
+    uint16_t* vA = vst0;
+    uint16_t* vB = vst0 + 32 * VST;
+    int ch = c0 + wave;
+    if (ch < c1) load_chunk(ch, kA, vA);
+    while (ch < c1) {
+      const int nx = ch + NW;
+      if (nx < c1) {
+        load_chunk(nx, kB, vB);
+        wait_vmem_le<KSTEPS + NPC>();  // chunk ch is in (registers and LDS)
+      } else {
+        wait_vmem();
+      }
+      compute_chunk(ch, kA, vA);
+      if (nx >= c1) break;
+      const int nx2 = nx + NW;
+      if (nx2 < c1) {
+        load_chunk(nx2, kA, vA);
+        wait_vmem_le<KSTEPS + NPC>();
+      } else {
+        wait_vmem();
+      }
+      compute_chunk(nx, kB, vB);
+      ch = nx2;
+    }
   }
 
   // ---- merge the waves of this workgroup (through LDS) -> split partial ----
@@ -365,21 +443,101 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     return;
   }
   merge_waves<D, DT>(wo, wml, NW, gg, ro, rml, split, nullptr, 0, scratch);
+  if (kMergeKernel) return;  // the split records are merged by decode_merge_kernel
 
   // ---- level 1: last workgroup of the group merges the group -------------------
   const int grp = split / kMergeGroup;
   const int gfirst = grp * kMergeGroup;
   const int gsize = min(kMergeGroup, p.nsplit - gfirst);
   unsigned* cnt0 = p.tickets + (long long)unit * (ngroups + 1);
-  if (!take_ticket(cnt0 + grp, (unsigned)gsize, &ticket_flag)) return;
+  // the ticket flag sits in the last word of the dynamic LDS, past the merge
+  // scratch (two workgroups of 80 KiB fill the 160 KiB of a CU exactly, so
+  // the kernel has no static LDS)
+  int* ticket_flag = reinterpret_cast<int*>(dyn_lds + p.lds_bytes) - 1;
+  if (!take_ticket(cnt0 + grp, (unsigned)gsize, ticket_flag)) return;
   if (ngroups == 1) {
     merge_global<D, DT>(ro, rml, gfirst, gsize, gg, 0, og, out_base, scratch);
     return;
   }
   merge_global<D, DT>(ro, rml, gfirst, gsize, gg, p.nsplit + grp, nullptr, 0, scratch);
   // ---- level 2: last group merger merges the groups and writes O -----------
-  if (!take_ticket(cnt0 + ngroups, (unsigned)ngroups, &ticket_flag)) return;
+  if (!take_ticket(cnt0 + ngroups, (unsigned)ngroups, ticket_flag)) return;
   merge_global<D, DT>(ro, rml, p.nsplit, ngroups, gg, 0, og, out_base, scratch);
+}
+
+// Second kernel: merges the nsplit (<= 256, see decode_num_splits) split
+// records of (unit, head g of the group) for 32 columns of O.  Thread t: columns 4 (t % 8) .. + 3, records
+// s = t / 8, t / 8 + 32, ...; the kernel boundary makes the records visible,
+// so plain loads suffice.
+constexpr int kMergeThreads = 256;
+template <int D, int DT>
+__global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p) {
+  using E = Elt<DT>;
+  __shared__ float w[256];
+  __shared__ float red[kMergeThreads / 64][2];
+  __shared__ f32x4 part[32][8];
+  const int unit = blockIdx.x, g = blockIdx.y, col0 = 32 * blockIdx.z;
+  const int HG = (p.gqa + 31) / 32;
+  const int hg = unit % HG;
+  const int bk = unit / HG;
+  const int b = bk / p.Hkv, hk = bk - b * p.Hkv;
+  const int gg = heads_in_group(p.gqa, hg);
+  if (g >= gg) return;
+  const int ns = p.nsplit;
+  const int ngroups = (ns + kMergeGroup - 1) / kMergeGroup;
+  const long long rec0 = (long long)unit * (ns + ngroups);  // this unit's first record
+  const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  // weights: M = max_s m_s, w_s = 2^(m_s - M), den = sum_s w_s l_s
+  float m = -__builtin_inff(), l = 0.f;
+  if (t < ns) {
+    m = p.part_ml[((rec0 + t) * gg + g) * 2 + 0];
+    l = p.part_ml[((rec0 + t) * gg + g) * 2 + 1];
+  }
+  float M = m;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  if (lane == 0) red[wv][0] = M;
+  __syncthreads();
+  M = red[0][0];
+#pragma unroll
+  for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[i][0]);
+  const float Mu = (M == -__builtin_inff()) ? 0.f : M;
+  const float f = t < ns ? fast_exp2(m - Mu) : 0.f;  // m = -inf -> 0
+  w[t] = f;
+  float dl = f * l;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) dl += __shfl_xor(dl, o);
+  if (lane == 0) red[wv][1] = dl;
+  __syncthreads();
+  float den = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMergeThreads / 64; ++i) den += red[i][1];
+  // columns: 8 threads x 4 columns, 32 record lanes
+  const int cg = t & 7, rl = t >> 3;
+  const float* po = p.part_o + (rec0 * gg + g) * D + col0 + 4 * cg;
+  f32x4 x[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int s = rl + 32 * k;
+    x[k] = s < ns ? *reinterpret_cast<const f32x4*>(po + (long long)s * gg * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int s = rl + 32 * k;
+    if (s < ns && w[s] != 0.f) acc += w[s] * x[k];
+  }
+  part[rl][cg] = acc;
+  __syncthreads();
+  if (t < 8) {
+    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
+    for (int r = 0; r < 32; ++r) sum += part[r][t];
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    const u32x2 pk = {E::pack2(sum[0] * inv, sum[1] * inv), E::pack2(sum[2] * inv, sum[3] * inv)};
+    uint16_t* og = static_cast<uint16_t*>(p.o);
+    const int hq = hk * p.gqa + 32 * hg + g;
+    *reinterpret_cast<u32x2*>(og + ((long long)b * p.Hq + hq) * D + col0 + 4 * t) = pk;
+  }
 }
 
 template <int D, int DT>
@@ -387,14 +545,22 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   const int HG = (p.gqa + 31) / 32;
   const int gg = min(32, p.gqa);
   const int ngroups = (p.nsplit + kMergeGroup - 1) / kMergeGroup;
-  const size_t stage = (size_t)kDecodeWaves * 32 * (D + kDVPad) * 2;
+  const size_t stage = (size_t)kDecodeWaves * 2 * 32 * (D + kDVPad) * 2;
   int nmax = kDecodeWaves;  // most records any merge step reads
   if (kMergeGroup > nmax) nmax = kMergeGroup;
   if (ngroups > nmax) nmax = ngroups;
-  const size_t merge = ((size_t)kDecodeWaves * gg * (D + 2) + (size_t)gg * (nmax + 2)) * 4;
+  const size_t merge = ((size_t)kDecodeWaves * gg * (D + 2) + (size_t)gg * (nmax + 2)) * 4 + 16;
   const size_t lds = stage > merge ? stage : merge;
+  DecodeParams q = p;
+  q.lds_bytes = (int)lds;
   dim3 grid(p.nsplit, p.B * p.Hkv * HG);
-  hipLaunchKernelGGL((decode_kernel<D, DT>), grid, dim3(kDecodeWaves * 64), lds, stream, p);
+  hipLaunchKernelGGL((decode_kernel<D, DT>), grid, dim3(kDecodeWaves * 64), lds, stream, q);
+  if (kMergeKernel && p.nsplit > 1) {
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((decode_merge_kernel<D, DT>), dim3(p.B * p.Hkv * HG, gg, D / 32),
+                       dim3(kMergeThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

@@ -63,6 +63,7 @@ struct DecodeParams {
   int B, Hq, Hkv, capacity;
   int gqa;
   int nsplit;          // splits per (b, kv head)
+  int lds_bytes;       // dynamic LDS of the launch (set by the launcher)
   float c_log2;
   int q_sign;
 };

@@ -43,9 +43,6 @@ namespace {
 
 constexpr int kKPad = 8;   // K LDS row = D + 8 elements (16-byte skew per row)
 constexpr int kVPad = 32;  // V LDS row = D + 32 elements (64-byte skew per row)
-// a byte offset past the end of any K/V buffer (their byte sizes are < 2^31):
-// buffer loads from it read zeros
-constexpr unsigned kPastEnd = 0x7FFFFFF0u;
 // 1 KiB LDS-image pieces per wave per tile copy: the K image of a 64-key tile
 // has 64 (D + 8) / 512 pieces, the V image 64 (D + 32) / 512; 4 waves share them
 constexpr int kDmaSlots = 5;
@@ -243,9 +240,7 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int u = 0; u < kDmaSlots; ++u) {
         if (gw + 4 * u < ni)
-          __builtin_amdgcn_raw_ptr_buffer_load_lds(
-              rs, (__attribute__((address_space(3))) void*)(dst + (gw + 4 * u) * 512), 16,
-              offs[u], t * BN * D * 2, 0, 0);
+          lds_dma16(rs, dst + (gw + 4 * u) * 512, offs[u], t * BN * D * 2);
       }
     };
 
