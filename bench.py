@@ -38,28 +38,32 @@ METRIC = "bf16 causal FA prefill TFLOP/s @Hq128/Hkv8/D128/Sq8192; % MFMA peak"
 PAGE_TFLOPS = 948.0              # prefill page, "Measured": persistent shipped default (MI355X)
 CALIB_BYTES = 256 << 20          # calibration copy: reads and writes 256 MiB
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_headline_traffic.json")
+DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_l65536_traffic.json")
 KERNEL_SOURCES = ["flash_attention_forward_fwd_amd/csrc/fa_prefill.hip",
+                  "flash_attention_forward_fwd_amd/csrc/fa_common.h",
+                  "flash_attention_forward_fwd_amd/csrc/fa_internal.h"]
+DECODE_SOURCES = ["flash_attention_forward_fwd_amd/csrc/fa_decode.hip",
                   "flash_attention_forward_fwd_amd/csrc/fa_common.h",
                   "flash_attention_forward_fwd_amd/csrc/fa_internal.h"]
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=None) -> str:
     h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
+    for rel in sources or KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
 
-def stored_traffic():
-    """HBM bytes per launch from the committed counter summary, or None when
-    it is absent or was taken on a different kernel source."""
+def stored_traffic(path=TRAFFIC_FILE, sources=None):
+    """HBM bytes per launch from a committed counter summary, or None when it
+    is absent or was taken on a different kernel source."""
     try:
-        with open(TRAFFIC_FILE) as f:
+        with open(path) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("kernel_source_hash") != kernel_source_hash():
+    if t.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
     return t.get("hbm_bytes_per_launch")
 
@@ -169,7 +173,8 @@ def bench_decode(fa, torch, steps, warmup):
     return {"metric": "bf16 Sq=1 split-KV decode GB/s @B1/Hq8/Hkv2/D128/L65536, NaN tail",
             "value": res["cold"]["GB_s"], "unit": "GB/s", "frac_of_hbm_peak":
             res["cold"]["GB_s"] / HBM_PEAK_GBS, "us_per_call": res["cold"]["us_per_call"],
-            "warm": res["warm"], "algorithmic_bytes": nbytes, "parity_worst_frac": frac}
+            "warm": res["warm"], "algorithmic_bytes": nbytes, "parity_worst_frac": frac,
+            "traffic": stored_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)}
 
 
 def main():
