@@ -23,6 +23,7 @@ from __future__ import annotations
 
 import argparse
 import hashlib
+import re
 import json
 import math
 import os
@@ -48,10 +49,15 @@ DECODE_SOURCES = ["flash_attention_forward_fwd_amd/csrc/fa_decode.hip",
 
 
 def kernel_source_hash(sources=None) -> str:
+    """Hash of the kernel sources with comments and blank space removed, so
+    that an edit of comments alone keeps the stored counter readings valid."""
     h = hashlib.sha256()
     for rel in sources or KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

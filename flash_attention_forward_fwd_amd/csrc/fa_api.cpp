@@ -205,6 +205,8 @@ fa_status_t fa_decode(const void* q, const void* kcache, const void* vcache,
   long long nq, ncache;
   if (!count4(B, Hq, D, 1, &nq) || !count4(B, capacity, Hkv, D, &ncache)) return FA_ERR_SHAPE;
   if (ncache > LLONG_MAX / 2 || (long long)B * Hkv > INT_MAX / 64) return FA_ERR_SHAPE;
+  // one batch's cache is addressed by 32-bit byte offsets from its base
+  if ((long long)capacity * Hkv * D * 2 > INT_MAX) return FA_ERR_SHAPE;
   if (B == 0) return FA_OK;
   if (!q || !kcache || !vcache || !valid_len || !o) return FA_ERR_NULL;
   for (const void* ptr : {q, kcache, vcache, static_cast<const void*>(o)})

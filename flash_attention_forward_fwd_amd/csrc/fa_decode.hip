@@ -14,12 +14,15 @@
 // one workgroup per run.  Each workgroup produces an unnormalised partial
 // (m, l, acc) per query head -- m the running max in the log2 domain, l the
 // sum of exp2(s - m), acc the exp2-weighted sum of V rows -- and the partials
-// are merged in the same launch:
+// are merged by
 //     M = max_s m_s,  O = sum_s 2^(m_s - M) acc_s / sum_s 2^(m_s - M) l_s
-// in two levels: the last workgroup to finish in each group of kMergeGroup
-// splits merges that group, and the last group merger merges the groups and
-// writes O.  "Last" is decided by a ticket counter per group that the merger
-// resets to zero, so the workspace is ready for the next call.
+// in a second kernel launched right after on the same stream (one workgroup
+// per (unit, head group, 32 columns of O)).  With kMergeKernel off the merge
+// runs inside the decode launch instead, in two levels: the last workgroup to
+// finish in each group of kMergeGroup splits merges that group, and the last
+// group merger merges the groups and writes O.  "Last" is decided by a ticket
+// counter per group that the merger resets to zero, so the workspace is ready
+// for the next call.  A single split skips the merge and writes O directly.
 //
 // Per wave and 32-token chunk, on the 32x32x16 matrix core (the query heads
 // that share a kv head form the MFMA N dimension, up to 32):

@@ -12,8 +12,11 @@
 //  * in persistent mode a grid of one workgroup per CU strides over the
 //    items ("Persistent (grid-stride) mode"), ordered kv-head-major when
 //    that still balances, so concurrently running items share K/V in L2;
-//  * KV tiles of 64 keys stream through double-buffered, row-padded LDS
-//    ("Baked-in levers": K rows padded against bank conflicts, V pad);
+//  * KV tiles of 64 keys stream through rings of three row-padded LDS
+//    slots ("Baked-in levers": K rows padded against bank conflicts, V pad),
+//    copied by 16-byte buffer loads that write LDS directly;
+//  * the two waves that share a SIMD run one phase apart (ping-pong): while
+//    one issues the tile's MFMAs the other runs its softmax;
 //  * below-diagonal tiles run mask-free, only tiles crossing the diagonal
 //    or the end of the keys evaluate the mask ("diagonal-only causal
 //    masking"); a wave skips tiles that are entirely masked for its rows.
@@ -24,15 +27,17 @@
 //    per lane (row = lane % 32) and 16 of the tile's keys per lane, so the
 //    row max and row sum need only one exchange with lane ^ 32.
 //  * exp2 online softmax: c = |scale| * log2(e) folded into one FMA per score,
-//    p = exp2(s*c - m) whose argument is <= 0 ("native exp2_fast").
+//    p = exp2(s*c - m_ref) ("native exp2_fast"), where the reference m_ref
+//    trails the running max by at most kRescaleTau, so the argument stays
+//    <= kRescaleTau.
 //  * O^T += V^T P^T: P is fed straight from the S accumulator registers as
 //    the B operand.  The contraction over keys is permuted to the order in
 //    which P already sits in registers, and V (A operand) is read from LDS
 //    with the gfx950 transposing read in that same permuted order -- no
 //    cross-lane relayout of P ("CK-1 transposed PV" describes the same
 //    idea).  O^T keeps one query row per lane, so the rescale by
-//    exp2(m_old - m_new) is lane-local and is skipped when no row of the
-//    wave raised its max (x * 1.0 == x, so skipping changes no bit).
+//    exp2(m_old - m_new) is lane-local; it runs only on tiles where some
+//    row of the wave moves its reference max.
 #include <type_traits>
 
 #include "fa_common.h"

@@ -75,6 +75,8 @@ typedef enum {
  * causal != 0 selects the bottom-right aligned causal mask.
  * scale multiplies the q.k dot products (1/sqrt(D) is the usual value).
  * B, Sq or Sk may be 0: B = 0 or Sq = 0 enqueues nothing; Sk = 0 writes O = 0.
+ * One (batch, kv head) of K or V must fit 32-bit byte offsets:
+ * Sk * D * 2 <= INT_MAX, else FA_ERR_SHAPE.
  */
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o,
                    int B, int Hq, int Hkv, int Sq, int Sk, int D,
@@ -134,6 +136,8 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int capacity);
  *               so it can be reused call after call on one stream.  Two calls
  *               in flight at once must not share a workspace.
  * Tokens at or past the valid length are never loaded.
+ * One batch's cache must fit 32-bit byte offsets: capacity * Hkv * D * 2 <=
+ * INT_MAX, else FA_ERR_SHAPE.
  */
 fa_status_t fa_decode(const void* q, const void* kcache, const void* vcache,
                       const int32_t* valid_len, int capacity, void* o,

@@ -59,6 +59,7 @@ def fwd(**kw):
     (dict(scale=float("inf")), SCALE), (dict(q=FAKE + 8), ALIGN), (dict(o=FAKE + 0x3000002), ALIGN),
     (dict(o=FAKE), ALIAS), (dict(o=FAKE + 0x1000000 + 256), ALIAS),
     (dict(B=1 << 20, Hq=1 << 10, Hkv=1 << 10, Sq=1 << 20), SHAPE),
+    (dict(Sk=1 << 23), SHAPE),
 ])
 def test_fwd_rejects_bad_arguments(kw, code):
     assert fwd(**kw) == code
@@ -101,6 +102,7 @@ def dec(**kw):
     (dict(ws=None), WS), (dict(wsb=16), WS), (dict(ws=FAKE + 0x5000000 + 128), WS),
     (dict(kc=FAKE + 0x1000000 + 2), ALIGN), (dict(vl=FAKE + 0x3000000 + 2), ALIGN),
     (dict(o=FAKE + 0x1000000), ALIAS), (dict(o=FAKE + 0x5000000), ALIAS),
+    (dict(cap=1 << 20, Hq=8, Hkv=8), SHAPE),
 ])
 def test_decode_rejects_bad_arguments(kw, code):
     assert dec(**kw) == code
