@@ -469,16 +469,19 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
 }
 
 // Second kernel: merges the nsplit (<= 256, see decode_num_splits) split
-// records of (unit, head g of the group) for 32 columns of O.  Thread t: columns 4 (t % 8) .. + 3, records
-// s = t / 8, t / 8 + 32, ...; the kernel boundary makes the records visible,
-// so plain loads suffice.
+// records of (unit, head g of the group) for 32 columns of O.  Thread t takes
+// columns 4 (t % 8) .. + 3 of records s = t / 8 + 32 k.  The kernel boundary
+// makes the records visible, so plain loads suffice; they do not depend on
+// the merge weights, so they are issued first, together with the (m, l)
+// loads, and the whole merge costs one memory round trip.
 constexpr int kMergeThreads = 256;
 template <int D, int DT>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p) {
   using E = Elt<DT>;
+  constexpr int NW = kMergeThreads / 64;
   __shared__ float w[256];
-  __shared__ float red[kMergeThreads / 64][2];
-  __shared__ f32x4 part[32][8];
+  __shared__ float red[NW][2];
+  __shared__ f32x4 part[NW][8];
   const int unit = blockIdx.x, g = blockIdx.y, col0 = 32 * blockIdx.z;
   const int HG = (p.gqa + 31) / 32;
   const int hg = unit % HG;
@@ -490,11 +493,20 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
   const int ngroups = (ns + kMergeGroup - 1) / kMergeGroup;
   const long long rec0 = (long long)unit * (ns + ngroups);  // this unit's first record
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
+  const int cg = t & 7, rl = t >> 3;
+  const float* po = p.part_o + (rec0 * gg + g) * D + col0 + 4 * cg;
+  f32x4 x[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) {
+    const int s = rl + 32 * k;
+    x[k] = s < ns ? *reinterpret_cast<const f32x4*>(po + (long long)s * gg * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+  }
   // weights: M = max_s m_s, w_s = 2^(m_s - M), den = sum_s w_s l_s
   float m = -__builtin_inff(), l = 0.f;
   if (t < ns) {
-    m = p.part_ml[((rec0 + t) * gg + g) * 2 + 0];
-    l = p.part_ml[((rec0 + t) * gg + g) * 2 + 1];
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(p.part_ml + ((rec0 + t) * gg + g) * 2);
+    m = ml[0];
+    l = ml[1];
   }
   float M = m;
 #pragma unroll
@@ -503,7 +515,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
   __syncthreads();
   M = red[0][0];
 #pragma unroll
-  for (int i = 1; i < kMergeThreads / 64; ++i) M = fmaxf(M, red[i][0]);
+  for (int i = 1; i < NW; ++i) M = fmaxf(M, red[i][0]);
   const float Mu = (M == -__builtin_inff()) ? 0.f : M;
   const float f = t < ns ? fast_exp2(m - Mu) : 0.f;  // m = -inf -> 0
   w[t] = f;
@@ -514,27 +526,26 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
   __syncthreads();
   float den = 0.f;
 #pragma unroll
-  for (int i = 0; i < kMergeThreads / 64; ++i) den += red[i][1];
-  // columns: 8 threads x 4 columns, 32 record lanes
-  const int cg = t & 7, rl = t >> 3;
-  const float* po = p.part_o + (rec0 * gg + g) * D + col0 + 4 * cg;
-  f32x4 x[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int s = rl + 32 * k;
-    x[k] = s < ns ? *reinterpret_cast<const f32x4*>(po + (long long)s * gg * D) : f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int i = 0; i < NW; ++i) den += red[i][1];
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int s = rl + 32 * k;
     if (s < ns && w[s] != 0.f) acc += w[s] * x[k];
   }
-  part[rl][cg] = acc;
+  // sum over the records: lanes of one column group inside a wave (lane % 8
+  // equal), then the waves
+#pragma unroll
+  for (int o = 8; o < 64; o <<= 1) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], o);
+  }
+  if (lane < 8) part[wv][lane] = acc;
   __syncthreads();
   if (t < 8) {
-    f32x4 sum = {0.f, 0.f, 0.f, 0.f};
-    for (int r = 0; r < 32; ++r) sum += part[r][t];
+    f32x4 sum = part[0][t];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) sum += part[i][t];
     const float inv = den > 0.f ? 1.0f / den : 0.f;
     const u32x2 pk = {E::pack2(sum[0] * inv, sum[1] * inv), E::pack2(sum[2] * inv, sum[3] * inv)};
     uint16_t* og = static_cast<uint16_t*>(p.o);
