@@ -6,10 +6,11 @@ A step is one fa_fwd call on the causal GQA prefill workload of the gfx950
 prefill page's headline row (B=1, Hq=128, Hkv=8, Sq=Sk=8192, D=128, bf16,
 inputs N(0,1), scale 1/sqrt(128)), with Q/K/V already resident in HBM.
 `value` is useful TFLOP/s: 4*D per admissible (query, key) pair, causal
-pairs only.  Before any figure is printed the same run checks sampled output
-rows against the CPU oracle.  The Sq=1 split-KV decode (B1/Hq8/Hkv2/D128,
-L = 65536, NaN-poisoned tail) is timed in the same run and reported as GB/s
-of algorithmic bytes in the "decode" object.
+pairs only.  The Sq=1 split-KV decode (B1/Hq8/Hkv2/D128, L = 65536,
+NaN-poisoned tail) is timed in the same run and reported as GB/s of
+algorithmic bytes in the "decode" object, and the packed varlen forward on a
+ragged batch (16 sequences of 256..8192 tokens, Hq32/Hkv8/D128, causal) in
+the "varlen" object.
 
 One JSON line is printed.  Besides the throughput it carries
   roofline      the prefill kernel's average launch time (HIP events on the
@@ -17,7 +18,12 @@ One JSON line is printed.  Besides the throughput it carries
                 HBM traffic measured by hardware counters when the stored
                 counter summary still matches the kernel source;
   cpu_baseline  the CPU oracle timed on this host over a bounded sample of
-                the same workload (whole query heads).
+                the same workload (whole query heads);
+  parity        the GPU outputs of that sample, of the decode call and of
+                sampled varlen rows against the same oracle (the CPU leg is
+                the only part of this script that runs the oracle; with
+                --cpu-sample-heads 0 both objects are null).
+The line is printed only if every parity check passes.
 """
 from __future__ import annotations
 
@@ -86,57 +92,81 @@ def host_bits(t):
     return t.cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
 
 
-def check_sampled_rows(q, k, v, out_bits, s, rng, heads=2, rows=24):
-    """Sampled rows of the output against the oracle; raises on a miss."""
+def worst_frac(got, ref):
+    """Largest |got - ref| / (1e-2 + 1e-2 |ref|); inf if got is not finite."""
+    import numpy as np
+    if not np.all(np.isfinite(got)):
+        return float("inf")
+    return float(np.max(np.abs(got - ref) / (1e-2 + 1e-2 * np.abs(ref)))) if got.size else 0.0
+
+
+def cpu_leg(prefill, decode, varlen, heads):
+    """The CPU oracle, as it stands, on this host.
+
+    Times it over `heads` whole query heads of the prefill workload (the CPU
+    baseline) and compares the GPU output of those heads with its result; also
+    runs it on the decode call and on sampled rows of the varlen batch and
+    compares those GPU outputs.  Raises SystemExit on any parity miss."""
     import numpy as np
 
-    import oracle
-    qf, kf, vf = oracle.widen(q, s.dtype), oracle.widen(k, s.dtype), oracle.widen(v, s.dtype)
-    worst = 0.0
-    for h in sorted(set(rng.integers(0, s.Hq, heads).tolist()) | {s.Hq - 1}):
-        rr = np.unique(np.concatenate([[0, s.Sq - 1], rng.integers(0, s.Sq, rows)]))
-        ref = oracle.attention_rows_ref(qf, kf, vf, s.causal, s.scale, 0, h, rr)
-        got = oracle.widen(out_bits[0, h, rr], s.dtype)
-        err = np.abs(got - ref)
-        frac = float(np.max(err / (1e-2 + 1e-2 * np.abs(ref))))
-        if not np.all(np.isfinite(got)) or frac > 1.0:
-            raise SystemExit(f"parity check failed on head {h}: worst fraction {frac}")
-        worst = max(worst, frac)
-    return worst
-
-
-def cpu_baseline(q, k, v, s, heads):
-    """Time the oracle (as it stands) over `heads` whole query heads."""
     import oracle
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
+    q, k, v, out_bits, s = prefill
     qf = oracle.widen(q[:, :heads], s.dtype)
     gqa = s.Hq // s.Hkv
     nkv = (heads + gqa - 1) // gqa
     kf, vf = oracle.widen(k[:, :nkv], s.dtype), oracle.widen(v[:, :nkv], s.dtype)
     # keep the GQA mapping of the full workload: head h reads kv head h // gqa
-    import numpy as np
     kk = np.repeat(kf, gqa, axis=1)[:, :heads]
     vv = np.repeat(vf, gqa, axis=1)[:, :heads]
     t0 = time.perf_counter()
-    oracle.attention_ref(qf, kk, vv, s.causal, s.scale)
+    ref = oracle.attention_ref(qf, kk, vv, s.causal, s.scale)
     dt = time.perf_counter() - t0
+    parity = {"prefill_heads": heads,
+              "prefill_worst_frac": worst_frac(oracle.widen(out_bits[:, :heads], s.dtype), ref)}
     flop = 4 * s.D * s.B * heads * s.admissible_pairs_per_head()
-    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    base = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
             "sample": f"{heads} of {s.Hq} query heads (B=1, Sq=Sk={s.Sq}, D={s.D}, causal), "
-                      f"{dt:.1f} s of float64 NumPy on {os.cpu_count()} visible CPUs",
-            "seconds": dt}
+                      f"{dt:.1f} s of float64 NumPy on {os.cpu_count()} visible CPUs"}
+    if decode is not None:
+        qb, kb, vb, L, scale, dout = decode
+        t0 = time.perf_counter()
+        dref = oracle.decode_ref(oracle.widen(qb, "bf16"), oracle.widen(kb, "bf16"),
+                                 oracle.widen(vb, "bf16"), [L], scale)
+        base["decode_seconds_per_token"] = round(time.perf_counter() - t0, 4)
+        parity["decode_worst_frac"] = worst_frac(oracle.widen(dout, "bf16"), dref)
+    if varlen is not None:
+        vq, vk, vv_, vout, vs = varlen
+        rng = np.random.default_rng(13)
+        worst = 0.0
+        qw, kw, vw = (oracle.widen(x, vs.dtype) for x in (vq, vk, vv_))
+        cu_q, cu_k = vs.cu_q, vs.cu_k
+        for b in sorted(set(rng.integers(0, vs.B, 3).tolist())):
+            q0, q1, k0, k1 = int(cu_q[b]), int(cu_q[b + 1]), int(cu_k[b]), int(cu_k[b + 1])
+            h = int(rng.integers(0, vs.Hq))
+            rows = np.unique(np.concatenate([[0, q1 - q0 - 1], rng.integers(0, q1 - q0, 16)]))
+            r = oracle.attention_rows_ref(qw[q0:q1].transpose(1, 0, 2)[None],
+                                          kw[k0:k1].transpose(1, 0, 2)[None],
+                                          vw[k0:k1].transpose(1, 0, 2)[None],
+                                          vs.causal, vs.scale, 0, h, rows)
+            worst = max(worst, worst_frac(oracle.widen(vout[q0 + rows, h], vs.dtype), r))
+        parity["varlen_sampled_worst_frac"] = worst
+    bad = {key: val for key, val in parity.items() if key.endswith("frac") and not val <= 1.0}
+    if bad:
+        raise SystemExit(f"parity check failed: {bad}")
+    for key in list(parity):
+        if key.endswith("frac"):
+            parity[key] = round(parity[key], 4)
+    return base, parity
 
 
 def bench_decode(fa, torch, steps, warmup):
     """Sq=1 decode at capacity 65536, L=65536, NaN tail: GB/s of algorithmic
     bytes, cold (rotating over more caches than the 256 MB MALL holds) and warm."""
-    import numpy as np
-
-    import oracle
     import workloads as wl
     B, Hq, Hkv, D, cap = 1, 8, 2, 128, 65536
     L = cap
@@ -153,12 +183,7 @@ def bench_decode(fa, torch, steps, warmup):
     scale = 1 / math.sqrt(D)
     fa.decode(q, kcs[0], vcs[0], vl, scale=scale, out=out, workspace=ws)
     torch.cuda.synchronize()
-    ref = oracle.decode_ref(oracle.widen(qb, "bf16"), oracle.widen(kb, "bf16"),
-                            oracle.widen(vb, "bf16"), [L], scale)
-    got = oracle.widen(host_bits(out), "bf16")
-    frac = float(np.max(np.abs(got - ref) / (1e-2 + 1e-2 * np.abs(ref))))
-    if not np.all(np.isfinite(got)) or frac > 1.0:
-        raise SystemExit(f"decode parity check failed: worst fraction {frac}")
+    first = host_bits(out)
     nbytes = 2 * L * Hkv * D * 2 + 2 * Hq * D * 2 + 4 * B
     res = {}
     stream = torch.cuda.current_stream()
@@ -179,8 +204,51 @@ def bench_decode(fa, torch, steps, warmup):
     return {"metric": "bf16 Sq=1 split-KV decode GB/s @B1/Hq8/Hkv2/D128/L65536, NaN tail",
             "value": res["cold"]["GB_s"], "unit": "GB/s", "frac_of_hbm_peak":
             res["cold"]["GB_s"] / HBM_PEAK_GBS, "us_per_call": res["cold"]["us_per_call"],
-            "warm": res["warm"], "algorithmic_bytes": nbytes, "parity_worst_frac": frac,
-            "traffic": stored_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)}
+            "warm": res["warm"], "algorithmic_bytes": nbytes,
+            "traffic": stored_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)}, \
+        (qb, kb, vb, L, scale, first)
+
+
+def bench_varlen(fa, torch, steps, warmup):
+    """The packed varlen forward on a ragged batch (16 causal sequences of
+    256..8192 tokens, Hq32/Hkv8/D128, bf16): useful TFLOP/s."""
+    import workloads as wl
+    s = wl.VARLEN
+    q, k, v = wl.varlen_inputs(s)
+    tq, tk, tv = dev(q, torch.bfloat16), dev(k, torch.bfloat16), dev(v, torch.bfloat16)
+    cq = torch.tensor(s.cu_q, dtype=torch.int32, device="cuda")
+    ck = torch.tensor(s.cu_k, dtype=torch.int32, device="cuda")
+    out = torch.empty_like(tq)
+    mq, mk = max(s.lens_q), max(s.lens_k)
+
+    def call():
+        fa.fwd_varlen(tq, tk, tv, cq, ck, mq, mk, causal=s.causal, scale=s.scale, out=out)
+
+    call()
+    torch.cuda.synchronize()
+    first = host_bits(out)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        call()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flop = s.useful_flop()
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"metric": "bf16 causal packed-varlen prefill TFLOP/s @16 seqs of 256..8192 tokens, "
+                      "Hq32/Hkv8/D128",
+            "value": round(tf, 2), "unit": "TFLOP/s",
+            "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+            "ms_per_call": round(ms, 4),
+            "config": {"workload": s.name, "B": s.B, "total_tokens": int(sum(s.lens_q)),
+                       "max_seqlen": mq, "Hq": s.Hq, "Hkv": s.Hkv, "D": s.D,
+                       "causal": s.causal, "useful_flop": flop}}, \
+        (q, k, v, first, s)
 
 
 def main():
@@ -191,6 +259,8 @@ def main():
     ap.add_argument("--cpu-sample-heads", type=int, default=24,
                     help="query heads the CPU oracle is timed on (0: no CPU baseline)")
     ap.add_argument("--decode", type=int, default=1, help="also time decode (1) or not (0)")
+    ap.add_argument("--varlen", type=int, default=1,
+                    help="also time the packed varlen forward (1) or not (0)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -198,7 +268,6 @@ def main():
               file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
     import torch
 
     import flash_attention_forward_fwd_amd as fa
@@ -213,7 +282,7 @@ def main():
     out = torch.empty_like(tq)
     fa.fwd(tq, tk, tv, causal=True, scale=s.scale, out=out)
     torch.cuda.synchronize()
-    worst = check_sampled_rows(q, k, v, host_bits(out), s, np.random.default_rng(11))
+    out_bits = host_bits(out)
 
     stream = torch.cuda.current_stream()
     for _ in range(args.warmup):
@@ -243,8 +312,13 @@ def main():
     torch.cuda.synchronize()
     del calib_src, calib_dst
 
-    dec = bench_decode(fa, torch, max(args.steps, 20), args.warmup) if args.decode else None
-    cpu = cpu_baseline(q, k, v, s, args.cpu_sample_heads) if args.cpu_sample_heads > 0 else None
+    dec, dec_data = (bench_decode(fa, torch, max(args.steps, 20), args.warmup) if args.decode
+                     else (None, None))
+    vl, vl_data = (bench_varlen(fa, torch, max(args.steps // 5, 5), min(args.warmup, 2))
+                   if args.varlen else (None, None))
+    cpu = parity = None
+    if args.cpu_sample_heads > 0:
+        cpu, parity = cpu_leg((q, k, v, out_bits, s), dec_data, vl_data, args.cpu_sample_heads)
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -264,12 +338,11 @@ def main():
                      "kernel": "prefill_kernel<128, bf16, causal>",
                      "avg_launch_ms": round(ms_kernel, 4),
                      "algorithmic_flop_per_launch": flop},
-        "parity": {"sampled_rows_worst_frac_of_bound": round(worst, 4)},
+        "parity": parity,
         "decode": dec,
+        "varlen": vl,
         "cpu_baseline": cpu,
     }
-    if cpu:
-        cpu.pop("seconds", None)
     print(json.dumps(line), flush=True)
 
 

@@ -15,7 +15,7 @@ import math
 
 from ._lib import (FA_BF16, FA_FP16, FaError, FwdPlan, check, lib)  # noqa: F401
 
-__all__ = ["fwd", "decode", "fwd_plan", "decode_workspace_bytes", "DecodeWorkspace", "FaError",
+__all__ = ["fwd", "fwd_varlen", "decode", "fwd_plan", "decode_workspace_bytes", "DecodeWorkspace", "FaError",
            "lib", "build"]
 
 
@@ -89,6 +89,49 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, ret
                       Sk, D, int(bool(causal)), float(scale), dt, stream)
     check(st, "fa_fwd")
     return out
+
+
+def fwd_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q: int, max_seqlen_k: int,
+               causal: bool = False, scale: float | None = None, out=None, return_lse=False):
+    """Attention over a batch of sequences packed along the token dimension:
+    q [total_q, Hq, D], k/v [total_k, Hkv, D], cu_seqlens_q/k int32 [B+1] on
+    the device (sequence b owns rows cu[b] .. cu[b+1]-1) -> o [total_q, Hq, D].
+
+    max_seqlen_q/k bound the sequence lengths (host integers).  Rows that
+    belong to no sequence are left as they are in `out` (uninitialised when
+    `out` is None).  With return_lse=True also returns the fp32 row
+    log-sum-exp [Hq, total_q]."""
+    torch = _torch()
+    if q.dim() != 3 or k.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k, v must be 3-D [total, H, D]")
+    total_q, Hq, D = q.shape
+    total_k, Hkv = k.shape[0], k.shape[1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("fwd_varlen needs GPU tensors")
+    if cu_seqlens_q.dim() != 1 or cu_seqlens_q.shape != cu_seqlens_k.shape:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B + 1]")
+    B = cu_seqlens_q.shape[0] - 1
+    if B < 0:
+        raise ValueError("cu_seqlens must hold at least one entry")
+    _check_tensor("cu_seqlens_q", cu_seqlens_q, (B + 1,), torch.int32, dev)
+    _check_tensor("cu_seqlens_k", cu_seqlens_k, (B + 1,), torch.int32, dev)
+    _check_tensor("k", k, (total_k, Hkv, D), q.dtype, dev)
+    _check_tensor("v", v, (total_k, Hkv, D), q.dtype, dev)
+    _check_tensor("q", q, (total_q, Hq, D), q.dtype, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, (total_q, Hq, D), q.dtype, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    lse = torch.empty((Hq, total_q), dtype=torch.float32, device=dev) if return_lse else None
+    st = lib().fa_fwd_varlen(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                             lse.data_ptr() if lse is not None else None,
+                             cu_seqlens_q.data_ptr(), cu_seqlens_k.data_ptr(), B, Hq, Hkv,
+                             total_q, total_k, int(max_seqlen_q), int(max_seqlen_k), D,
+                             int(bool(causal)), float(scale), _dtype_code(q), _stream_ptr(q))
+    check(st, "fa_fwd_varlen")
+    return (out, lse) if return_lse else out
 
 
 def fwd_plan(B, Hq, Hkv, Sq, Sk, D, causal) -> dict:

@@ -27,6 +27,8 @@ _F = ctypes.c_float
 SIGNATURES = {
     "fa_fwd": (_I, [_P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_fwd_lse": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P]),
+    "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
+                           _P]),
     "fa_fwd_plan": (_I, [_I, _I, _I, _I, _I, _I, _I, _P]),
     "fa_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _I, _P, ctypes.c_size_t,

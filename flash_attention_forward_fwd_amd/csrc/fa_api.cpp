@@ -146,14 +146,89 @@ fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
   p.lse = lse;
   p.q_bstride = (long long)Hq * Sq * D;
   p.kv_bstride = (long long)Hkv * Sk * D;
+  p.cu_q = nullptr;
+  p.cu_k = nullptr;
+  p.total_q = 0;
+  p.total_k = 0;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.Sq = Sq;
   p.Sk = Sk;
   p.gqa = Hq / Hkv;
-  p.kv_off = Sk - Sq;
   p.nqb = (Sq + fa::kPrefillBM - 1) / fa::kPrefillBM;
+  p.work_items = plan.work_items;
+  p.hkv_major = plan.hkv_major;
+  p.persistent = plan.persistent;
+  fold_scale(scale, &p.c_log2, &p.q_sign);
+  const hipError_t e = fa::launch_prefill(p, D, dtype, causal != 0, plan.grid,
+                                          static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t varlen_impl(const void* q, const void* k, const void* v, void* o, float* lse,
+                        const int32_t* cu_q, const int32_t* cu_k, int B, int Hq, int Hkv,
+                        int total_q, int total_k, int max_sq, int max_sk, int D, int causal,
+                        float scale, int dtype) {
+  if (total_q < 0 || total_k < 0) return FA_ERR_SHAPE;
+  // the launch plan of a dense batch of B sequences of the maximum lengths
+  fa_fwd_plan_t plan;
+  const fa_status_t ps = plan_prefill(B, Hq, Hkv, max_sq, max_sk, D, causal, &plan);
+  if (ps != FA_OK) return ps;
+  if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  long long nq, nkv;
+  if (!count4(total_q, Hq, D, 1, &nq) || !count4(total_k, Hkv, D, 1, &nkv)) return FA_ERR_SHAPE;
+  if (nq > LLONG_MAX / 4 || nkv > LLONG_MAX / 2) return FA_ERR_SHAPE;
+  // one sequence's K or V is addressed with 32-bit byte offsets
+  if ((long long)max_sk * Hkv * D * 2 > INT_MAX) return FA_ERR_SHAPE;
+  if (B > 0 && (!cu_q || !cu_k)) return FA_ERR_NULL;
+  if (nq > 0 && (!q || !o)) return FA_ERR_NULL;
+  if (nkv > 0 && (!k || !v)) return FA_ERR_NULL;
+  for (const void* ptr : {q, k, v, static_cast<const void*>(o), static_cast<const void*>(lse)})
+    if (ptr && !aligned16(ptr)) return FA_ERR_ALIGN;
+  for (const void* ptr : {static_cast<const void*>(cu_q), static_cast<const void*>(cu_k)})
+    if (ptr && (reinterpret_cast<uintptr_t>(ptr) & 3u) != 0) return FA_ERR_ALIGN;
+  const long long ob = nq * 2, kb = nkv * 2, lb = (long long)total_q * Hq * 4, cb = (B + 1LL) * 4;
+  if (overlaps(o, ob, q, ob) || overlaps(o, ob, k, kb) || overlaps(o, ob, v, kb) ||
+      overlaps(o, ob, cu_q, cb) || overlaps(o, ob, cu_k, cb))
+    return FA_ERR_ALIAS;
+  if (lse && (overlaps(lse, lb, q, ob) || overlaps(lse, lb, k, kb) || overlaps(lse, lb, v, kb) ||
+              overlaps(lse, lb, o, ob) || overlaps(lse, lb, cu_q, cb) ||
+              overlaps(lse, lb, cu_k, cb)))
+    return FA_ERR_ALIAS;
+  return FA_OK;
+}
+
+fa_status_t launch_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int32_t* cu_q, const int32_t* cu_k, int B, int Hq, int Hkv,
+                          int total_q, int total_k, int max_sq, int max_sk, int D, int causal,
+                          float scale, int dtype, void* stream) {
+  const fa_status_t st = varlen_impl(q, k, v, o, lse, cu_q, cu_k, B, Hq, Hkv, total_q, total_k,
+                                     max_sq, max_sk, D, causal, scale, dtype);
+  if (st != FA_OK) return st;
+  if (B == 0 || max_sq == 0 || total_q == 0) return FA_OK;
+  fa_fwd_plan_t plan;
+  plan_prefill(B, Hq, Hkv, max_sq, max_sk, D, causal, &plan);
+  fa::PrefillParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.q_bstride = 0;
+  p.kv_bstride = 0;
+  p.cu_q = cu_q;
+  p.cu_k = cu_k;
+  p.total_q = total_q;
+  p.total_k = total_k;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Sq = max_sq;
+  p.Sk = max_sk;
+  p.gqa = Hq / Hkv;
+  p.nqb = (max_sq + fa::kPrefillBM - 1) / fa::kPrefillBM;
   p.work_items = plan.work_items;
   p.hkv_major = plan.hkv_major;
   p.persistent = plan.persistent;
@@ -166,6 +241,15 @@ fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
 }  // namespace
 
 extern "C" {
+
+fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B,
+                          int Hq, int Hkv, int total_q, int total_k, int max_seqlen_q,
+                          int max_seqlen_k, int D, int causal, float scale, int dtype,
+                          void* stream) {
+  return launch_varlen(q, k, v, o, lse, cu_seqlens_q, cu_seqlens_k, B, Hq, Hkv, total_q, total_k,
+                       max_seqlen_q, max_seqlen_k, D, causal, scale, dtype, stream);
+}
 
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
                    int Sq, int Sk, int D, int causal, float scale, int dtype, void* stream) {

@@ -30,9 +30,14 @@ struct PrefillParams {
   float* lse;          // nullptr unless the LSE variant runs
   long long q_bstride; // elements between batches of q / o  (Hq * Sq * D)
   long long kv_bstride;// elements between batches of k / v  (Hkv * Sk * D)
+  // varlen (packed [total, H, D] tensors): device int32[B + 1] row offsets of
+  // the sequences; nullptr for the dense layout.  Sq / Sk are then the
+  // maximum sequence lengths.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int total_q, total_k;
   int B, Hq, Hkv, Sq, Sk;
   int gqa;             // Hq / Hkv
-  int kv_off;          // Sk - Sq (bottom-right causal offset)
   int nqb;             // ceil(Sq / BM)
   int work_items;      // nqb * Hq * B
   int hkv_major;       // work-item order

@@ -129,7 +129,68 @@ __device__ __forceinline__ void decode_item(const PrefillParams& p, int w, int& 
   }
 }
 
-template <int D, int DT, bool CAUSAL, bool LSE>
+// Packed varlen schedule.  The work items are the non-empty (sequence, query
+// head, query block) triples, in the dense order: block level descending (a
+// causal block's cost grows with its index whatever sequence it belongs to),
+// kv head outermost when kv-head-major.  Empty blocks of short sequences are
+// left out, so the persistent round-robin sees a list of items of steadily
+// falling cost, as in the dense case, instead of long and short sequences
+// pinned to fixed workgroups (page "Dense flash-attention prefill (gfx950 /
+// MI355X)", TODO / follow-ups: per-sequence load balance of the varlen path).
+// Every wave derives an item from the per-sequence block counts in LDS.
+constexpr int kVarlenMaxSeqs = 4096;  // batches up to this size use the table
+
+// sequences with more than L query blocks
+__device__ __forceinline__ int seqs_above(const uint16_t* nqb, int B, int L, int lane) {
+  int n = 0;
+  for (int c = 0; c < B; c += 64) {
+    const bool on = c + lane < B && nqb[c + lane] > L;
+    n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(on));
+  }
+  return n;
+}
+
+// index of the j-th (from 0) sequence with more than L query blocks
+__device__ __forceinline__ int nth_seq_above(const uint16_t* nqb, int B, int L, int j, int lane) {
+  for (int c = 0; c < B; c += 64) {
+    const bool on = c + lane < B && nqb[c + lane] > L;
+    const unsigned long long m = __builtin_amdgcn_ballot_w64(on);
+    const int cnt = __builtin_popcountll(m);
+    if (j < cnt) {
+      // the lane whose bit is the j-th set bit has j set bits below it
+      const int below = __builtin_amdgcn_mbcnt_hi((unsigned)(m >> 32),
+                                                  __builtin_amdgcn_mbcnt_lo((unsigned)m, 0u));
+      return c + __builtin_ctzll(__builtin_amdgcn_ballot_w64(on && below == j));
+    }
+    j -= cnt;
+  }
+  return 0;
+}
+
+// work item w of the compacted varlen list -> (sequence, query head, block)
+__device__ __forceinline__ void varlen_item(const PrefillParams& p, const uint16_t* nqb,
+                                            int total_blocks, int w, int lane, int& b, int& hq,
+                                            int& qb) {
+  const int per = p.hkv_major ? p.gqa : p.Hq;  // items per (sequence, block)
+  int r = w, hk = 0;
+  if (p.hkv_major) {
+    const int per_kv = total_blocks * p.gqa;
+    hk = w / per_kv;
+    r = w - hk * per_kv;
+  }
+  int L = p.nqb - 1;
+  for (; L > 0; --L) {
+    const int n = seqs_above(nqb, p.B, L, lane) * per;
+    if (r < n) break;
+    r -= n;
+  }
+  const int j = r / per, m = r - j * per;
+  b = nth_seq_above(nqb, p.B, L, j, lane);
+  qb = L;
+  hq = p.hkv_major ? hk * p.gqa + m : m;
+}
+
+template <int D, int DT, bool CAUSAL, bool LSE, bool VARLEN>
 __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams p) {
   using E = Elt<DT>;
@@ -165,42 +226,89 @@ void prefill_kernel(PrefillParams p) {
   uint16_t* __restrict__ og = static_cast<uint16_t*>(p.o);
   const float c = p.c_log2;
 
+  // varlen: query blocks per sequence, and the compacted item count
+  __shared__ uint16_t nqb_tab[VARLEN ? kVarlenMaxSeqs : 1];
+  int work_items = p.work_items, total_blocks = 0;
+  const bool compact = VARLEN && p.B <= kVarlenMaxSeqs && p.nqb <= 0xFFFF;
+  if constexpr (VARLEN) {
+    if (compact) {
+      for (int i = tid; i < p.B; i += NT) {
+        const int lo = min(max(p.cu_q[i], 0), p.total_q);
+        const int hi = min(max(p.cu_q[i + 1], lo), p.total_q);
+        nqb_tab[i] = (uint16_t)((min(hi - lo, p.Sq) + BM - 1) / BM);
+      }
+      __syncthreads();
+      int t = 0;
+      for (int i = lane; i < p.B; i += 64) t += nqb_tab[i];
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
+      total_blocks = uniform(t);
+      work_items = total_blocks * p.Hq;
+    }
+  }
+
   const int NP = gridDim.x;
   for (int round = 0;; ++round) {
     int w;
     if (p.persistent) {
-      if (round * NP >= p.work_items) break;
+      if (round * NP >= work_items) break;
       // snake order: even rounds ascend, odd rounds descend, so every CTA
       // pairs a heavy item with a light one
       w = round * NP + ((round & 1) ? (NP - 1 - (int)blockIdx.x) : (int)blockIdx.x);
-      if (w >= p.work_items) continue;
+      if (w >= work_items) continue;
     } else {
       if (round > 0) break;
       w = blockIdx.x;
+      if (w >= work_items) break;
     }
     int b, hq, qb;
-    decode_item(p, w, b, hq, qb);
+    if (compact) varlen_item(p, nqb_tab, total_blocks, w, lane, b, hq, qb);
+    else decode_item(p, w, b, hq, qb);
     const int hk = hq / p.gqa;
     const int q0 = qb * BM;
     const int rw0 = q0 + wave * 32;  // first row of this wave
     const int row = rw0 + li;        // this lane's query row
-    const long long qbase = (long long)b * p.q_bstride + (long long)hq * p.Sq * D;
-    const long long kvbase = (long long)b * p.kv_bstride + (long long)hk * p.Sk * D;
+    // this item's sequence: Sq query rows and Sk keys, row strides QRS / KRS
+    // elements.  Dense: [B, H, S, D] tensors.  Varlen: packed [total, H, D]
+    // tensors whose sequence b spans rows [cu[b], cu[b + 1]), with offsets
+    // clamped to [0, total] and lengths to the declared maxima (p.Sq, p.Sk),
+    // so no index leaves the tensors whatever the offsets hold.
+    int Sq = p.Sq, Sk = p.Sk, q_lo = 0;
+    long long qbase, kvbase;
+    int QRS = D, KRS = D;
+    if constexpr (VARLEN) {
+      q_lo = min(max(p.cu_q[b], 0), p.total_q);
+      const int q_hi = min(max(p.cu_q[b + 1], q_lo), p.total_q);
+      const int k_lo = min(max(p.cu_k[b], 0), p.total_k);
+      const int k_hi = min(max(p.cu_k[b + 1], k_lo), p.total_k);
+      Sq = uniform(min(q_hi - q_lo, p.Sq));
+      Sk = uniform(min(k_hi - k_lo, p.Sk));
+      q_lo = uniform(q_lo);
+      QRS = p.Hq * D;
+      KRS = p.Hkv * D;
+      qbase = (long long)q_lo * QRS + (long long)hq * D;
+      kvbase = (long long)uniform(k_lo) * KRS + (long long)hk * D;
+      if (q0 >= Sq) continue;  // query block past the end of this sequence
+    } else {
+      qbase = (long long)b * p.q_bstride + (long long)hq * Sq * D;
+      kvbase = (long long)b * p.kv_bstride + (long long)hk * Sk * D;
+    }
+    const int kv_off = Sk - Sq;  // bottom-right causal offset
 
     // keys [0, kv_end) are streamed for the item; this wave needs [0, wave_end)
-    int kv_end = p.Sk, wave_end = p.Sk;
+    int kv_end = Sk, wave_end = Sk;
     if (CAUSAL) {
-      kv_end = min(max(min(p.Sq, q0 + BM) + p.kv_off, 0), p.Sk);
-      wave_end = min(max(min(p.Sq, rw0 + 32) + p.kv_off, 0), p.Sk);
+      kv_end = min(max(min(Sq, q0 + BM) + kv_off, 0), Sk);
+      wave_end = min(max(min(Sq, rw0 + 32) + kv_off, 0), Sk);
     }
-    if (rw0 >= p.Sq) wave_end = 0;
+    if (rw0 >= Sq) wave_end = 0;
     const int ntiles = (kv_end + BN - 1) / BN;
     // tiles [0, free_tiles) are admissible for every row of this wave, tiles
     // [0, main_tiles) for every row of the workgroup (the mask-free body)
-    int free_tiles = p.Sk / BN, main_tiles = p.Sk / BN;
+    int free_tiles = Sk / BN, main_tiles = Sk / BN;
     if (CAUSAL) {
-      free_tiles = min(free_tiles, max(rw0 + p.kv_off + 1, 0) / BN);
-      main_tiles = min(main_tiles, max(q0 + p.kv_off + 1, 0) / BN);
+      free_tiles = min(free_tiles, max(rw0 + kv_off + 1, 0) / BN);
+      main_tiles = min(main_tiles, max(q0 + kv_off + 1, 0) / BN);
     }
     main_tiles = min(main_tiles, ntiles);
 
@@ -209,7 +317,7 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) {
       u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < p.Sq) x = gload16(qg + qbase + (long long)row * D + 16 * kk + 8 * lh);
+      if (row < Sq) x = gload16(qg + qbase + (long long)row * QRS + 16 * kk + 8 * lh);
       if (p.q_sign < 0) x ^= 0x80008000u;
       if (p.q_sign == 0) x = u32x4{0u, 0u, 0u, 0u};
       qr[kk] = x;
@@ -227,25 +335,27 @@ void prefill_kernel(PrefillParams p) {
     // copy holds no registers and issues no LDS stores.  A tile's LDS image,
     // padding included, is cut into 1 KiB pieces, one per load; image chunk
     // c is row c / RC, column c % RC, and padding columns (>= CH) load from
-    // an offset past the buffer, which reads zeros.  Buffer descriptors span
-    // this (batch, kv head)'s K and V, so rows >= Sk read zeros too.
+    // an offset past the buffer, which reads zeros.  Buffer descriptors end
+    // right after this (sequence, kv head)'s last key row, so rows >= Sk read
+    // zeros too.
+    const int kv_bytes = Sk > 0 ? ((Sk - 1) * KRS + D) * 2 : 0;
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(kg + kvbase), (short)0, p.Sk * D * 2, kBufferFlags);
+        const_cast<uint16_t*>(kg + kvbase), (short)0, kv_bytes, kBufferFlags);
     const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(vg + kvbase), (short)0, p.Sk * D * 2, kBufferFlags);
+        const_cast<uint16_t*>(vg + kvbase), (short)0, kv_bytes, kBufferFlags);
     const int gw = wave % (kPrefillWaves / 2);  // wave index inside its group
     // lane's global byte offset for load u of this wave (loads gw, gw+4, ...)
     auto dma_offset = [&](int rc, int u) -> unsigned {
       const int cidx = 64 * (gw + 4 * u) + lane;
       const int rr = cidx / rc, cc = cidx - rr * rc;
-      return cc < CH ? (unsigned)((rr * D + cc * 8) * 2) : kPastEnd;
+      return cc < CH ? (unsigned)((rr * KRS + cc * 8) * 2) : kPastEnd;
     };
     auto dma_tile = [&](__amdgpu_buffer_rsrc_t rs, uint16_t* dst, int t, int ni,
                         const unsigned* offs) {
 #pragma unroll
       for (int u = 0; u < kDmaSlots; ++u) {
         if (gw + 4 * u < ni)
-          lds_dma16(rs, dst + (gw + 4 * u) * 512, offs[u], t * BN * D * 2);
+          lds_dma16(rs, dst + (gw + 4 * u) * 512, offs[u], t * BN * KRS * 2);
       }
     };
 
@@ -353,8 +463,8 @@ void prefill_kernel(PrefillParams p) {
     auto slot = [](int tile) { return uniform(tile % NBUF); };
     // tile t is needed by this wave iff t*BN < wave_end; sub-tile keys past
     // free_keys need the mask for some row of this wave
-    int free_keys = p.Sk;
-    if (CAUSAL) free_keys = min(free_keys, max(rw0 + p.kv_off + 1, 0));
+    int free_keys = Sk;
+    if (CAUSAL) free_keys = min(free_keys, max(rw0 + kv_off + 1, 0));
     const int nphase = ntiles > 0 ? 2 * ntiles + 2 : 0;
     // phases [4, main_end) run straight-line steps: every tile they touch
     // (t-1, t with t <= main_tiles - 2 for the lagging group) is needed by
@@ -433,8 +543,8 @@ void prefill_kernel(PrefillParams p) {
           if (!ALL && t * BN + BN > free_keys) {
             // register r of S0 (S1) holds key t*BN + 4*lh + off(r) (+32): keep
             // keys <= lim = min(row + Sk - Sq, Sk - 1) of this lane's row
-            int lim = p.Sk - 1;
-            if (CAUSAL) lim = min(lim, row + p.kv_off);
+            int lim = Sk - 1;
+            if (CAUSAL) lim = min(lim, row + kv_off);
             lim -= t * BN + 4 * lh;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -480,8 +590,8 @@ void prefill_kernel(PrefillParams p) {
     // ---- epilogue: O = O^T / l, rows < Sq --------------------------------------
     const float l_tot = pair_sum(l_run);
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    if (row < p.Sq) {
-      uint16_t* orow = og + qbase + (long long)row * D + 4 * lh;
+    if (row < Sq) {
+      uint16_t* orow = og + qbase + (long long)row * QRS + 4 * lh;
 #pragma unroll
       for (int dt = 0; dt < DTILES; ++dt) {
 #pragma unroll
@@ -493,26 +603,33 @@ void prefill_kernel(PrefillParams p) {
       }
       if (LSE && lh == 0) {
         const float lse = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -__builtin_inff();
-        p.lse[((long long)b * p.Hq + hq) * p.Sq + row] = lse;
+        if constexpr (VARLEN) p.lse[(long long)hq * p.total_q + q_lo + row] = lse;
+        else p.lse[((long long)b * p.Hq + hq) * Sq + row] = lse;
       }
     }
   }
 }
 
-template <int D, int DT, bool CAUSAL, bool LSE>
+template <int D, int DT, bool CAUSAL, bool LSE, bool VARLEN>
 hipError_t launch_one(const PrefillParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<D, DT, CAUSAL, LSE>), dim3(grid), dim3(kPrefillWaves * 64), 0,
-                     stream, p);
+  hipLaunchKernelGGL((prefill_kernel<D, DT, CAUSAL, LSE, VARLEN>), dim3(grid),
+                     dim3(kPrefillWaves * 64), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int D, int DT, bool CAUSAL>
+hipError_t launch_c(const PrefillParams& p, int grid, hipStream_t stream) {
+  const bool lse = p.lse != nullptr;
+  if (p.cu_q != nullptr)
+    return lse ? launch_one<D, DT, CAUSAL, true, true>(p, grid, stream)
+               : launch_one<D, DT, CAUSAL, false, true>(p, grid, stream);
+  return lse ? launch_one<D, DT, CAUSAL, true, false>(p, grid, stream)
+             : launch_one<D, DT, CAUSAL, false, false>(p, grid, stream);
 }
 
 template <int D, int DT>
 hipError_t launch_dt(const PrefillParams& p, bool causal, int grid, hipStream_t stream) {
-  const bool lse = p.lse != nullptr;
-  if (causal) return lse ? launch_one<D, DT, true, true>(p, grid, stream)
-                         : launch_one<D, DT, true, false>(p, grid, stream);
-  return lse ? launch_one<D, DT, false, true>(p, grid, stream)
-             : launch_one<D, DT, false, false>(p, grid, stream);
+  return causal ? launch_c<D, DT, true>(p, grid, stream) : launch_c<D, DT, false>(p, grid, stream);
 }
 
 }  // namespace

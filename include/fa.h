@@ -96,6 +96,37 @@ fa_status_t fa_fwd_lse(const void* q, const void* k, const void* v, void* o, flo
                        int causal, float scale, int dtype, void* stream);
 
 /*
+ * fa_fwd_varlen -- fa_fwd over a batch of sequences of different lengths,
+ * packed along the token dimension (the packed varlen path, cu_seqlens_q/kv,
+ * that the page "Dense flash-attention prefill (gfx950 / MI355X)" names
+ * under TODO / follow-ups).
+ *   q   : [total_q, Hq,  D]  queries of all sequences, back to back
+ *   k   : [total_k, Hkv, D]  keys
+ *   v   : [total_k, Hkv, D]  values
+ *   o   : [total_q, Hq,  D]  output (written for the rows of every sequence)
+ *   lse : NULL, or [Hq, total_q] float32: natural-log row log-sum-exp as in
+ *         fa_fwd_lse (-inf for a row with no admissible key)
+ *   cu_seqlens_q, cu_seqlens_k : device int32[B + 1]; sequence b owns query
+ *         rows [cu_seqlens_q[b], cu_seqlens_q[b+1]) and key rows
+ *         [cu_seqlens_k[b], cu_seqlens_k[b+1]).  They are read on the device
+ *         only.  Offsets are clamped to [0, total] and lengths to
+ *         max_seqlen_q / max_seqlen_k, so malformed offsets give unspecified
+ *         values but never an access outside the tensors.  Rows that belong
+ *         to no sequence are not written.
+ *   max_seqlen_q, max_seqlen_k : upper bounds of the sequence lengths; the
+ *         launch is planned for a dense batch of B sequences of these lengths
+ *         and work items past the end of a shorter sequence exit at once.
+ * Within sequence b attention is that of fa_fwd with Sq = its query length
+ * and Sk = its key length (bottom-right causal mask when causal != 0).
+ * Limits: max_seqlen_k * Hkv * D * 2 <= INT_MAX, else FA_ERR_SHAPE.
+ */
+fa_status_t fa_fwd_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                          int B, int Hq, int Hkv, int total_q, int total_k,
+                          int max_seqlen_q, int max_seqlen_k, int D,
+                          int causal, float scale, int dtype, void* stream);
+
+/*
  * fa_fwd_plan -- the launch plan fa_fwd would use for a shape (host only, no
  * HIP call).  Exposed so the schedule can be inspected and tested.
  */

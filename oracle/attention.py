@@ -28,6 +28,9 @@ to rounding order):
   past L is never read (decode PR page: device valid length, contiguous
   token-major KV; review: the unused tail is outside the logical sequence).
 
+Packed variable-length batches (varlen_ref) apply the same definition to
+each sequence of the batch separately.
+
 Pins: every function here is checked in tests/test_oracle_pins.py against
 brute force on tiny inputs, closed forms (identical keys -> prefix mean of V,
 one dominant key -> that V row, causal row 0 -> V[0], probability rows sum
@@ -208,3 +211,35 @@ def lse_ref(q: np.ndarray, k: np.ndarray, causal: bool, scale: float) -> np.ndar
             tot = np.where(allowed, np.exp(s - ms[:, None]), 0.0).sum(axis=1)
             out[b, h] = np.where(ok, ms + np.log(np.where(ok, tot, 1.0)), -np.inf)
     return out
+
+
+# ----------------------------------------------------------------------------
+# packed variable-length batches
+# ----------------------------------------------------------------------------
+def varlen_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, causal: bool,
+               scale: float, with_lse: bool = False):
+    """Attention over sequences packed along the token axis (the packed varlen
+    path with cu_seqlens_q / cu_seqlens_k named on the page "Dense
+    flash-attention prefill (gfx950 / MI355X)", TODO / follow-ups).
+
+    q: [total_q, Hq, D]; k, v: [total_k, Hkv, D]; cu_q, cu_k: int [B + 1],
+    non-decreasing offsets.  Sequence b is plain attention of query rows
+    cu_q[b] .. cu_q[b+1]-1 against key rows cu_k[b] .. cu_k[b+1]-1, with the
+    bottom-right causal mask of its own two lengths.  Returns O
+    [total_q, Hq, D] (float64) -- NaN in rows that belong to no sequence --
+    and, with with_lse, LSE [Hq, total_q] (NaN likewise)."""
+    total_q, Hq, _ = q.shape
+    out = np.full((total_q, Hq, v.shape[2]), np.nan)
+    lse = np.full((Hq, total_q), np.nan)
+    for b in range(len(cu_q) - 1):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
+        if q1 <= q0:
+            continue
+        qs = q[q0:q1].transpose(1, 0, 2)[None]  # [1, Hq, Sq_b, D]
+        ks = k[k0:k1].transpose(1, 0, 2)[None]  # [1, Hkv, Sk_b, D]
+        vs = v[k0:k1].transpose(1, 0, 2)[None]
+        out[q0:q1] = attention_ref(qs, ks, vs, causal, scale)[0].transpose(1, 0, 2)
+        if with_lse:
+            lse[:, q0:q1] = lse_ref(qs, ks, causal, scale)[0]
+    return (out, lse) if with_lse else out

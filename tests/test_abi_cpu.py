@@ -29,8 +29,8 @@ def declared_functions():
 def test_library_loads_and_exports_header_functions():
     lib = fa.lib()
     names = declared_functions()
-    assert set(names) == {"fa_fwd", "fa_fwd_lse", "fa_fwd_plan", "fa_decode_workspace_bytes",
-                          "fa_decode", "fa_status_string"}
+    assert set(names) == {"fa_fwd", "fa_fwd_lse", "fa_fwd_varlen", "fa_fwd_plan",
+                          "fa_decode_workspace_bytes", "fa_decode", "fa_status_string"}
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES
@@ -81,6 +81,34 @@ def test_fwd_lse_requires_lse_pointer():
     st = lib.fa_fwd_lse(FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000, FAKE + 16, 1,
                         4, 2, 128, 128, 128, 1, 0.1, 0, None)
     assert st == ALIAS
+
+
+def varlen(**kw):
+    a = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, o=FAKE + 0x3000000, lse=None,
+             cq=FAKE + 0x4000000, ck=FAKE + 0x4000100, B=2, Hq=4, Hkv=2, tq=300, tk=500, mq=200,
+             mk=300, D=128, causal=1, scale=0.1, dtype=0, stream=None)
+    a.update(kw)
+    return fa.lib().fa_fwd_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cq"], a["ck"],
+                                  a["B"], a["Hq"], a["Hkv"], a["tq"], a["tk"], a["mq"], a["mk"],
+                                  a["D"], a["causal"], a["scale"], a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k=None), NULL), (dict(o=None), NULL), (dict(cq=None), NULL),
+    (dict(ck=None), NULL), (dict(B=-1), SHAPE), (dict(tq=-1), SHAPE), (dict(tk=-1), SHAPE),
+    (dict(mq=-1), SHAPE), (dict(mk=-2), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(D=80), UNSUP),
+    (dict(dtype=5), UNSUP), (dict(scale=float("nan")), SCALE), (dict(q=FAKE + 8), ALIGN),
+    (dict(cq=FAKE + 0x4000002), ALIGN), (dict(lse=FAKE + 0x5000004), ALIGN),
+    (dict(o=FAKE), ALIAS), (dict(o=FAKE + 0x4000000 - 64), ALIAS),
+    (dict(lse=FAKE + 0x3000000), ALIAS), (dict(mk=1 << 21, Hkv=4), SHAPE),
+])
+def test_varlen_rejects_bad_arguments(kw, code):
+    assert varlen(**kw) == code
+
+
+def test_varlen_empty_needs_no_pointers():
+    assert varlen(B=0, cq=None, ck=None, q=None, o=None, tq=0) == OK
+    assert varlen(tq=0, q=None, o=None) == OK
 
 
 def dec(**kw):

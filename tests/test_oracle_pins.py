@@ -286,6 +286,60 @@ def test_lse_against_brute_force_and_torch():
 
 
 # ----------------------------------------------------------------------------
+# packed variable-length batches
+# ----------------------------------------------------------------------------
+def _pack(x):
+    """[B, H, S, D] -> [B*S, H, D] (sequences back to back)."""
+    B, H, S, D = x.shape
+    return x.transpose(0, 2, 1, 3).reshape(B * S, H, D)
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_varlen_equal_lengths_is_the_dense_batch(causal):
+    B, Hq, Hkv, Sq, Sk, D = 3, 4, 2, 9, 13, 8
+    q, k, v = rnd((B, Hq, Sq, D), 141), rnd((B, Hkv, Sk, D), 142), rnd((B, Hkv, Sk, D), 143)
+    cu_q, cu_k = np.arange(B + 1) * Sq, np.arange(B + 1) * Sk
+    got, lse = oracle.varlen_ref(_pack(q), _pack(k), _pack(v), cu_q, cu_k, causal, 0.4, True)
+    np.testing.assert_allclose(got, _pack(oracle.attention_ref(q, k, v, causal, 0.4)), atol=1e-12)
+    want_lse = oracle.lse_ref(q, k, causal, 0.4)  # [B, Hq, Sq]
+    np.testing.assert_allclose(lse, want_lse.transpose(1, 0, 2).reshape(Hq, B * Sq), atol=1e-12)
+
+
+def test_varlen_ragged_against_brute_force():
+    # lengths 3/0/5 queries against 4/2/6 keys, rows 8..9 belong to no sequence
+    Hq, Hkv, D = 2, 1, 3
+    cu_q, cu_k = np.array([0, 3, 3, 8]), np.array([0, 4, 6, 12])
+    q, k, v = rnd((10, Hq, D), 144), rnd((12, Hkv, D), 145), rnd((12, Hkv, D), 146)
+    for causal in (False, True):
+        got = oracle.varlen_ref(q, k, v, cu_q, cu_k, causal, 0.7)
+        for b in range(3):
+            q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+            want = brute(q[q0:q1].transpose(1, 0, 2)[None], k[k0:k1].transpose(1, 0, 2)[None],
+                         v[k0:k1].transpose(1, 0, 2)[None], causal, 0.7)[0].transpose(1, 0, 2)
+            np.testing.assert_allclose(got[q0:q1], want, atol=1e-12)
+        assert np.all(np.isnan(got[8:]))
+
+
+def test_varlen_sequences_do_not_mix():
+    Hq, Hkv, D = 2, 2, 4
+    cu_q, cu_k = np.array([0, 5, 12]), np.array([0, 7, 10])
+    q, k, v = rnd((12, Hq, D), 147), rnd((10, Hkv, D), 148), rnd((10, Hkv, D), 149)
+    base = oracle.varlen_ref(q, k, v, cu_q, cu_k, True, 0.5)
+    k2, v2 = k.copy(), v.copy()
+    k2[7:] += 3.0
+    v2[7:] -= 2.0
+    other = oracle.varlen_ref(q, k2, v2, cu_q, cu_k, True, 0.5)
+    np.testing.assert_array_equal(base[:5], other[:5])   # sequence 0 untouched
+    assert not np.allclose(base[5:], other[5:])           # sequence 1 sees its own keys
+    # swapping the two sequences swaps the outputs
+    qs = np.concatenate([q[5:], q[:5]])
+    ks, vs = np.concatenate([k[7:], k[:7]]), np.concatenate([v[7:], v[:7]])
+    sw = oracle.varlen_ref(qs, ks, vs, np.array([0, 7, 12]), np.array([0, 3, 10]), True, 0.5)
+    np.testing.assert_allclose(sw[:7], base[5:], atol=1e-12)
+    np.testing.assert_allclose(sw[7:], base[:5], atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
 # the pages' own reproduction case (decode review): NaN tail, L = 1 -> V[0]
 # ----------------------------------------------------------------------------
 def test_golden_decode_nan_tail_case():
@@ -347,3 +401,40 @@ def test_unmutated_oracle_passes_compact_pins():
 @pytest.mark.parametrize("mutation", MUTATIONS, ids=[m[1][:30] for m in MUTATIONS])
 def test_planted_mistake_is_caught(mutation):
     assert not _pins_pass(_mutant(*mutation))
+
+
+VARLEN_MUTATIONS = [
+    ("k0, k1 = int(cu_k[b]), int(cu_k[b + 1])", "k0, k1 = int(cu_q[b]), int(cu_q[b + 1])"),
+    ("qs = q[q0:q1].transpose(1, 0, 2)[None]",
+     "qs = q[q0:q1].reshape(1, q.shape[1], q1 - q0, -1)"),             # token/head mix-up
+    ("vs = v[k0:k1].transpose(1, 0, 2)[None]", "vs = k[k0:k1].transpose(1, 0, 2)[None]"),
+    ("for b in range(len(cu_q) - 1):", "for b in range(len(cu_q) - 2):"),  # last sequence lost
+]
+
+
+def _varlen_pins_pass(ns):
+    """The ragged brute-force pin, rerun on a mutant."""
+    try:
+        Hq, Hkv, D = 2, 1, 3
+        cu_q, cu_k = np.array([0, 3, 3, 8]), np.array([0, 4, 6, 12])
+        q, k, v = rnd((8, Hq, D), 144), rnd((12, Hkv, D), 145), rnd((12, Hkv, D), 146)
+        for causal in (False, True):
+            got = ns["varlen_ref"](q, k, v, cu_q, cu_k, causal, 0.7)
+            for b in range(3):
+                q0, q1, k0, k1 = cu_q[b], cu_q[b + 1], cu_k[b], cu_k[b + 1]
+                want = brute(q[q0:q1].transpose(1, 0, 2)[None], k[k0:k1].transpose(1, 0, 2)[None],
+                             v[k0:k1].transpose(1, 0, 2)[None], causal, 0.7)[0].transpose(1, 0, 2)
+                if not np.allclose(got[q0:q1], want, atol=1e-12, rtol=0):
+                    return False
+        return True
+    except Exception:
+        return False
+
+
+def test_unmutated_varlen_oracle_passes_its_pin():
+    assert _varlen_pins_pass(_mutant("", ""))
+
+
+@pytest.mark.parametrize("mutation", VARLEN_MUTATIONS, ids=[m[1][:30] for m in VARLEN_MUTATIONS])
+def test_planted_varlen_mistake_is_caught(mutation):
+    assert not _varlen_pins_pass(_mutant(*mutation))

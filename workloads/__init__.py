@@ -152,6 +152,70 @@ def decode_query(s: DecodeShape, seed: int) -> np.ndarray:
     return normal_bits((s.B, s.Hq, s.D), seed, s.dtype)
 
 
+def admissible_pairs(Sq: int, Sk: int, causal: bool) -> int:
+    """Number of (query, key) pairs the mask admits for one head of one
+    sequence: row i admits min(Sk, max(0, i + Sk - Sq + 1)) keys when causal."""
+    if not causal:
+        return Sq * Sk
+    i = np.arange(Sq, dtype=np.int64)
+    return int(np.minimum(Sk, np.maximum(0, i + (Sk - Sq) + 1)).sum())
+
+
+def ragged_lengths(n: int, lo: int, hi: int, seed: int) -> tuple:
+    """n sequence lengths drawn uniformly from [lo, hi] (seeded)."""
+    return tuple(int(x) for x in np.random.default_rng(seed).integers(lo, hi + 1, n))
+
+
+@dataclasses.dataclass(frozen=True)
+class VarlenShape:
+    """A batch of sequences packed along the token axis ([total, H, D]),
+    sequence b owning rows cu[b] .. cu[b+1]-1 (the packed varlen path with
+    cu_seqlens_q / cu_seqlens_k of the prefill page's follow-ups)."""
+    name: str
+    lens_q: tuple
+    lens_k: tuple
+    Hq: int
+    Hkv: int
+    D: int
+    causal: bool
+    dtype: str = BF16
+    seed_base: int = 6000
+
+    @property
+    def scale(self) -> float:
+        return 1.0 / math.sqrt(self.D)
+
+    @property
+    def cu_q(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.lens_q)]).astype(np.int64)
+
+    @property
+    def cu_k(self) -> np.ndarray:
+        return np.concatenate([[0], np.cumsum(self.lens_k)]).astype(np.int64)
+
+    @property
+    def B(self) -> int:
+        return len(self.lens_q)
+
+    def useful_flop(self) -> int:
+        """4 * D * Hq per admissible pair, summed over the sequences."""
+        return 4 * self.D * self.Hq * sum(admissible_pairs(a, b, self.causal)
+                                          for a, b in zip(self.lens_q, self.lens_k))
+
+    def algorithmic_bytes(self) -> int:
+        e = 2
+        return e * self.D * (2 * self.Hq * sum(self.lens_q) + 2 * self.Hkv * sum(self.lens_k))
+
+
+def varlen_inputs(s: VarlenShape):
+    """(q, k, v) uint16 bit arrays, q:[total_q,Hq,D], k,v:[total_k,Hkv,D]."""
+    tq, tk = int(sum(s.lens_q)), int(sum(s.lens_k))
+    q = normal_bits((tq, s.Hq, s.D), s.seed_base + 0, s.dtype)
+    k = normal_bits((tk, s.Hkv, s.D), s.seed_base + 1, s.dtype)
+    v = normal_bits((tk, s.Hkv, s.D), s.seed_base + 2, s.dtype)
+    return q, k, v
+
+
 # The pages' workloads, as sizes.  seed_base = 1000 * config number.
 TINY = PrefillShape("tiny_causal_gqa_b1_hq2_hkv1_s256_d64", 1, 2, 1, 256, 256, 64, True,
                     seed_base=1000)
@@ -176,6 +240,11 @@ SWEEP = tuple(PrefillShape(f"causal_gqa_b1_hq128_hkv8_s{s}_d128", 1, 128, 8, s, 
 
 DECODE_SMALL = DecodeShape("decode_b1_hq8_hkv2_d128_cap128", 1, 8, 2, 128, 128)
 DECODE_LARGE = DecodeShape("decode_b1_hq8_hkv2_d128_cap65536", 1, 8, 2, 128, 65536)
+
+# a ragged batch for the packed varlen path: 16 sequences of 256..8192 tokens
+_VARLEN_LENS = ragged_lengths(16, 256, 8192, 6000)
+VARLEN = VarlenShape("varlen_causal_b16_len256to8192_hq32_hkv8_d128", _VARLEN_LENS, _VARLEN_LENS,
+                     32, 8, 128, True, seed_base=6000)
 
 PREFILL_CONFIGS = (TINY, MHA_CAUSAL, MHA_FULL, MHA_FP16, GQA_D128, GQA_D64, RAGGED_D128,
                    RAGGED_D64, HEADLINE) + SWEEP
