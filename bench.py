@@ -201,10 +201,29 @@ def bench_decode(fa, torch, steps, warmup):
         torch.cuda.synchronize()
         us = e0.elapsed_time(e1) * 1e3 / steps
         res[mode] = {"us_per_call": us, "GB_s": nbytes / (us * 1e-6) / 1e9}
+    # the same caches read as pools of 256-token pages through a page table
+    # (identity mapping), cold
+    P = 256
+    kps = [kc.view(cap // P, P, Hkv, D) for kc in kcs]
+    vps = [vc.view(cap // P, P, Hkv, D) for vc in vcs]
+    table = torch.arange(cap // P, dtype=torch.int32, device="cuda").view(1, cap // P)
+    for i in range(warmup):
+        fa.decode_paged(q, kps[i % copies], vps[i % copies], table, vl, scale=scale, out=out,
+                        workspace=ws)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        fa.decode_paged(q, kps[i % copies], vps[i % copies], table, vl, scale=scale, out=out,
+                        workspace=ws)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    res["paged"] = {"page_size": P, "us_per_call": us, "GB_s": nbytes / (us * 1e-6) / 1e9}
     return {"metric": "bf16 Sq=1 split-KV decode GB/s @B1/Hq8/Hkv2/D128/L65536, NaN tail",
             "value": res["cold"]["GB_s"], "unit": "GB/s", "frac_of_hbm_peak":
             res["cold"]["GB_s"] / HBM_PEAK_GBS, "us_per_call": res["cold"]["us_per_call"],
-            "warm": res["warm"], "algorithmic_bytes": nbytes,
+            "warm": res["warm"], "paged_cold": res["paged"], "algorithmic_bytes": nbytes,
             "traffic": stored_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)}, \
         (qb, kb, vb, L, scale, first)
 

@@ -15,7 +15,7 @@ import math
 
 from ._lib import (FA_BF16, FA_FP16, FaError, FwdPlan, check, lib)  # noqa: F401
 
-__all__ = ["fwd", "fwd_varlen", "decode", "fwd_plan", "decode_workspace_bytes", "DecodeWorkspace", "FaError",
+__all__ = ["fwd", "fwd_varlen", "decode", "decode_paged", "fwd_plan", "decode_workspace_bytes", "DecodeWorkspace", "FaError",
            "lib", "build"]
 
 
@@ -191,4 +191,45 @@ def decode(q, kcache, vcache, valid_len, causal: bool = False, scale: float | No
                          cap, out.data_ptr(), B, Hq, Hkv, D, int(bool(causal)), float(scale),
                          _dtype_code(q), workspace.ptr, workspace.nbytes, _stream_ptr(q))
     check(st, "fa_decode")
+    return out
+
+
+def decode_paged(q, k_pages, v_pages, page_table, valid_len, causal: bool = False,
+                 scale: float | None = None, out=None, workspace: DecodeWorkspace | None = None):
+    """Sq=1 attention over a paged cache: q [B,Hq,D], k_pages/v_pages
+    [num_pages, page_size, Hkv, D], page_table int32 [B, pages_per_seq] and
+    valid_len int32[B] on the device -> o [B,Hq,D].  Token t of batch b is
+    row t % page_size of page page_table[b, t // page_size]; page_size must be
+    a multiple of 32."""
+    torch = _torch()
+    if q.dim() != 3 or k_pages.dim() != 4 or page_table.dim() != 2:
+        raise ValueError("q must be [B, Hq, D], the pools [num_pages, page_size, Hkv, D] and "
+                         "page_table [B, pages_per_seq]")
+    B, Hq, D = q.shape
+    num_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
+    pages_per_seq = page_table.shape[1]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("decode_paged needs GPU tensors")
+    _check_tensor("q", q, (B, Hq, D), q.dtype, dev)
+    _check_tensor("k_pages", k_pages, (num_pages, page_size, Hkv, D), q.dtype, dev)
+    _check_tensor("v_pages", v_pages, (num_pages, page_size, Hkv, D), q.dtype, dev)
+    _check_tensor("page_table", page_table, (B, pages_per_seq), torch.int32, dev)
+    _check_tensor("valid_len", valid_len, (B,), torch.int32, dev)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_tensor("out", out, (B, Hq, D), q.dtype, dev)
+    cap = pages_per_seq * page_size
+    if workspace is None:
+        workspace = DecodeWorkspace(B, Hq, Hkv, D, cap, device=dev)
+    if workspace.key != (B, Hq, Hkv, D, cap):
+        raise ValueError("workspace was sized for other shapes")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = lib().fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
+                               page_table.data_ptr(), valid_len.data_ptr(), page_size,
+                               pages_per_seq, num_pages, out.data_ptr(), B, Hq, Hkv, D,
+                               int(bool(causal)), float(scale), _dtype_code(q), workspace.ptr,
+                               workspace.nbytes, _stream_ptr(q))
+    check(st, "fa_decode_paged")
     return out

@@ -238,6 +238,78 @@ fa_status_t launch_varlen(const void* q, const void* k, const void* v, void* o, 
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
 }
 
+// Sq = 1 decode over a contiguous cache (page_table == nullptr) or a paged
+// pool; all checks before any HIP call.
+constexpr long long kMaxPagedCapacity = 1LL << 21;  // tokens a paged sequence may span
+
+fa_status_t decode_impl(const void* q, const void* kc, const void* vc, const int32_t* valid_len,
+                        const int32_t* page_table, int page_size, int pages_per_seq,
+                        int num_pages, int capacity, void* o, int B, int Hq, int Hkv, int D,
+                        float scale, int dtype, void* workspace, size_t workspace_bytes,
+                        void* stream) {
+  const bool paged = page_size > 0;
+  if (B < 0 || Hq < 1 || Hkv < 1 || capacity < 1) return FA_ERR_SHAPE;
+  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  long long nq, ncache, ntable = 0;
+  if (!count4(B, Hq, D, 1, &nq)) return FA_ERR_SHAPE;
+  if (paged) {
+    if (!count4(num_pages, page_size, Hkv, D, &ncache) || !count4(B, pages_per_seq, 1, 1, &ntable))
+      return FA_ERR_SHAPE;
+    // one page is addressed by 32-bit byte offsets from its base
+    if ((long long)page_size * Hkv * D * 2 > INT_MAX) return FA_ERR_SHAPE;
+  } else {
+    if (!count4(B, capacity, Hkv, D, &ncache)) return FA_ERR_SHAPE;
+    // one batch's cache is addressed by 32-bit byte offsets from its base
+    if ((long long)capacity * Hkv * D * 2 > INT_MAX) return FA_ERR_SHAPE;
+  }
+  if (ncache > LLONG_MAX / 2 || ntable > LLONG_MAX / 4 || (long long)B * Hkv > INT_MAX / 64)
+    return FA_ERR_SHAPE;
+  if (B == 0) return FA_OK;
+  if (!q || !kc || !vc || !valid_len || !o || (paged && !page_table)) return FA_ERR_NULL;
+  for (const void* ptr : {q, kc, vc, static_cast<const void*>(o)})
+    if (!aligned16(ptr)) return FA_ERR_ALIGN;
+  if ((reinterpret_cast<uintptr_t>(valid_len) & 3u) != 0) return FA_ERR_ALIGN;
+  if (paged && (reinterpret_cast<uintptr_t>(page_table) & 3u) != 0) return FA_ERR_ALIGN;
+  const size_t need = fa::decode_workspace_layout(B, Hq, Hkv, D, capacity, nullptr, nullptr);
+  if (!workspace || workspace_bytes < need ||
+      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return FA_ERR_WORKSPACE;
+  const long long ob = nq * 2, cb = ncache * 2;
+  if (overlaps(o, ob, q, ob) || overlaps(o, ob, kc, cb) || overlaps(o, ob, vc, cb) ||
+      overlaps(o, ob, valid_len, (long long)B * 4) || overlaps(o, ob, workspace, (long long)need) ||
+      overlaps(o, ob, page_table, ntable * 4))
+    return FA_ERR_ALIAS;
+
+  fa::DecodeParams p;
+  p.q = q;
+  p.k = kc;
+  p.v = vc;
+  p.valid_len = valid_len;
+  p.o = o;
+  size_t off_ml = 0, off_tickets = 0;
+  fa::decode_workspace_layout(B, Hq, Hkv, D, capacity, &off_ml, &off_tickets);
+  char* ws = static_cast<char*>(workspace);
+  p.part_o = reinterpret_cast<float*>(ws);
+  p.part_ml = reinterpret_cast<float*>(ws + off_ml);
+  p.tickets = reinterpret_cast<unsigned*>(ws + off_tickets);
+  p.page_table = paged ? page_table : nullptr;
+  p.page_size = page_size;
+  p.pages_per_seq = pages_per_seq;
+  p.num_pages = num_pages;
+  p.gqa = Hq / Hkv;
+  p.nsplit = fa::decode_num_splits(B, Hkv, capacity);
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.capacity = capacity;
+  fold_scale(scale, &p.c_log2, &p.q_sign);
+  const hipError_t e = fa::launch_decode(p, D, dtype, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -281,51 +353,23 @@ fa_status_t fa_decode(const void* q, const void* kcache, const void* vcache,
                       int D, int causal, float scale, int dtype, void* workspace,
                       size_t workspace_bytes, void* stream) {
   (void)causal;  // at Sq = 1 the bottom-right causal mask admits every valid token
-  if (B < 0 || Hq < 1 || Hkv < 1 || capacity < 1) return FA_ERR_SHAPE;
-  if (Hq % Hkv != 0) return FA_ERR_SHAPE;
-  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
-  if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale)) return FA_ERR_SCALE;
-  long long nq, ncache;
-  if (!count4(B, Hq, D, 1, &nq) || !count4(B, capacity, Hkv, D, &ncache)) return FA_ERR_SHAPE;
-  if (ncache > LLONG_MAX / 2 || (long long)B * Hkv > INT_MAX / 64) return FA_ERR_SHAPE;
-  // one batch's cache is addressed by 32-bit byte offsets from its base
-  if ((long long)capacity * Hkv * D * 2 > INT_MAX) return FA_ERR_SHAPE;
-  if (B == 0) return FA_OK;
-  if (!q || !kcache || !vcache || !valid_len || !o) return FA_ERR_NULL;
-  for (const void* ptr : {q, kcache, vcache, static_cast<const void*>(o)})
-    if (!aligned16(ptr)) return FA_ERR_ALIGN;
-  if ((reinterpret_cast<uintptr_t>(valid_len) & 3u) != 0) return FA_ERR_ALIGN;
-  const size_t need = fa::decode_workspace_layout(B, Hq, Hkv, D, capacity, nullptr, nullptr);
-  if (!workspace || workspace_bytes < need ||
-      (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return FA_ERR_WORKSPACE;
-  const long long ob = nq * 2, cb = ncache * 2;
-  if (overlaps(o, ob, q, ob) || overlaps(o, ob, kcache, cb) || overlaps(o, ob, vcache, cb) ||
-      overlaps(o, ob, valid_len, (long long)B * 4) || overlaps(o, ob, workspace, (long long)need))
-    return FA_ERR_ALIAS;
+  return decode_impl(q, kcache, vcache, valid_len, nullptr, 0, 0, 0, capacity, o, B, Hq, Hkv, D,
+                     scale, dtype, workspace, workspace_bytes, stream);
+}
 
-  fa::DecodeParams p;
-  p.q = q;
-  p.k = kcache;
-  p.v = vcache;
-  p.valid_len = valid_len;
-  p.o = o;
-  size_t off_ml = 0, off_tickets = 0;
-  fa::decode_workspace_layout(B, Hq, Hkv, D, capacity, &off_ml, &off_tickets);
-  char* ws = static_cast<char*>(workspace);
-  p.part_o = reinterpret_cast<float*>(ws);
-  p.part_ml = reinterpret_cast<float*>(ws + off_ml);
-  p.tickets = reinterpret_cast<unsigned*>(ws + off_tickets);
-  p.gqa = Hq / Hkv;
-  p.nsplit = fa::decode_num_splits(B, Hkv, capacity);
-  p.B = B;
-  p.Hq = Hq;
-  p.Hkv = Hkv;
-  p.capacity = capacity;
-  fold_scale(scale, &p.c_log2, &p.q_sign);
-  const hipError_t e = fa::launch_decode(p, D, dtype, static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                            const int32_t* page_table, const int32_t* valid_len, int page_size,
+                            int pages_per_seq, int num_pages, void* o, int B, int Hq, int Hkv,
+                            int D, int causal, float scale, int dtype, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  (void)causal;
+  if (page_size < 32 || page_size % 32 != 0 || pages_per_seq < 1 || num_pages < 1)
+    return FA_ERR_SHAPE;
+  const long long capacity = (long long)pages_per_seq * page_size;
+  if (capacity > kMaxPagedCapacity) return FA_ERR_SHAPE;
+  return decode_impl(q, k_pages, v_pages, valid_len, page_table, page_size, pages_per_seq,
+                     num_pages, (int)capacity, o, B, Hq, Hkv, D, scale, dtype, workspace,
+                     workspace_bytes, stream);
 }
 
 const char* fa_status_string(int status) {

@@ -226,7 +226,7 @@ __device__ __forceinline__ bool take_ticket(unsigned* counter, unsigned total, i
   return *lds_flag != 0;
 }
 
-template <int D, int DT>
+template <int D, int DT, bool PAGED>
 __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_kernel(DecodeParams p) {
   using E = Elt<DT>;
   constexpr int NW = kDecodeWaves;
@@ -263,7 +263,23 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   const uint16_t* __restrict__ vg = static_cast<const uint16_t*>(p.v);
   const float c = p.c_log2;
   const long long tok_stride = (long long)p.Hkv * D;  // elements between tokens
-  const long long cache_base = (long long)b * p.capacity * tok_stride + (long long)hk * D;
+  const long long cache_base =
+      PAGED ? (long long)hk * D : (long long)b * p.capacity * tok_stride + (long long)hk * D;
+
+  // Paged cache: logical page lp of batch b is physical page
+  // page_table[b][lp] of a pool [num_pages, page_size, Hkv, D]; page_size is
+  // a multiple of 32, so a 32-token chunk never straddles two pages.  Lane j
+  // of a wave holds the physical page of the wave's j-th chunk (a wave has at
+  // most 64 chunks; the host bounds the capacity for that).  Entries are
+  // clamped to the pool, so no table value leads outside it.
+  int my_page = 0;
+  if constexpr (PAGED) {
+    const int chj = c0 + wave + NW * lane;
+    if (chj < c1) {
+      const int e = p.page_table[(long long)b * p.pages_per_seq + (chj * 32) / p.page_size];
+      my_page = min(max(e, 0), p.num_pages - 1);
+    }
+  }
 
   // Q of the group's heads as the B operand (lane: head li, d = 16kk + 8lh + e)
   u32x4 qr[KSTEPS];
@@ -309,13 +325,28 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   float m_run = -__builtin_inff(), l_run = 0.f;
 
   auto load_chunk = [&](int ch, u32x4 (&kr)[KSTEPS], uint16_t* vbuf) {
-    const int soff = ch * 32 * (int)tok_stride * 2;
+    int soff;
+    __amdgpu_buffer_rsrc_t kc = krs, vc = vrs;
+    if constexpr (!PAGED) {
+      soff = ch * 32 * (int)tok_stride * 2;
+    } else {
+      // this chunk's page as a buffer range ending at token L
+      const int lp = (ch * 32) / p.page_size;
+      const int phys = __builtin_amdgcn_readlane(my_page, (ch - c0 - wave) / NW);
+      const int in_page = min(p.page_size, L - lp * p.page_size);
+      const long long base = (long long)phys * p.page_size * tok_stride + cache_base;
+      kc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kg + base), (short)0,
+                                             (int)(in_page * tok_stride * 2), kBufferFlags);
+      vc = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vg + base), (short)0,
+                                             (int)(in_page * tok_stride * 2), kBufferFlags);
+      soff = (ch * 32 - lp * p.page_size) * (int)tok_stride * 2;
+    }
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk)
-      kr[kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(krs, k_off + 32 * kk, soff, 0));
+      kr[kk] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(kc, k_off + 32 * kk, soff, 0));
 #pragma unroll
     for (int i = 0; i < NPC; ++i)
-      lds_dma16(vrs, vbuf + i * 512, voffs[i], soff);
+      lds_dma16(vc, vbuf + i * 512, voffs[i], soff);
   };
   auto compute_chunk = [&](int ch, const u32x4 (&kr)[KSTEPS], const uint16_t* vbuf) {
     const int tok0 = ch * 32;
@@ -554,7 +585,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
   }
 }
 
-template <int D, int DT>
+template <int D, int DT, bool PAGED>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   const int HG = (p.gqa + 31) / 32;
   const int gg = min(32, p.gqa);
@@ -568,7 +599,7 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   DecodeParams q = p;
   q.lds_bytes = (int)lds;
   dim3 grid(p.nsplit, p.B * p.Hkv * HG);
-  hipLaunchKernelGGL((decode_kernel<D, DT>), grid, dim3(kDecodeWaves * 64), lds, stream, q);
+  hipLaunchKernelGGL((decode_kernel<D, DT, PAGED>), grid, dim3(kDecodeWaves * 64), lds, stream, q);
   if (kMergeKernel && p.nsplit > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -576,6 +607,11 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
                        dim3(kMergeThreads), 0, stream, p);
   }
   return hipGetLastError();
+}
+
+template <int D, int DT>
+hipError_t launch_p(const DecodeParams& p, hipStream_t stream) {
+  return p.page_table ? launch_d<D, DT, true>(p, stream) : launch_d<D, DT, false>(p, stream);
 }
 
 }  // namespace
@@ -614,9 +650,9 @@ size_t decode_workspace_layout(int B, int Hq, int Hkv, int D, int capacity, size
 
 hipError_t launch_decode(const DecodeParams& p, int D, int dtype, hipStream_t stream) {
   if (D == 128) {
-    return dtype == kBF16 ? launch_d<128, kBF16>(p, stream) : launch_d<128, kFP16>(p, stream);
+    return dtype == kBF16 ? launch_p<128, kBF16>(p, stream) : launch_p<128, kFP16>(p, stream);
   }
-  return dtype == kBF16 ? launch_d<64, kBF16>(p, stream) : launch_d<64, kFP16>(p, stream);
+  return dtype == kBF16 ? launch_p<64, kBF16>(p, stream) : launch_p<64, kFP16>(p, stream);
 }
 
 }  // namespace fa

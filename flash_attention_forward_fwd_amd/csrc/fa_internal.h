@@ -65,6 +65,12 @@ struct DecodeParams {
   float* part_o;       // [B*Hkv][nsplit][gqa][D] fp32
   float* part_ml;      // [B*Hkv][nsplit][gqa][2] fp32 (m in log2 domain, l)
   unsigned* tickets;   // [B*Hkv]
+  // paged cache: device int32 [B][pages_per_seq] physical page of each
+  // logical page of a pool [num_pages][page_size][Hkv][D]; nullptr for the
+  // contiguous [B][capacity][Hkv][D] cache.  capacity = pages_per_seq *
+  // page_size when paged.
+  const int32_t* page_table;
+  int page_size, pages_per_seq, num_pages;
   int B, Hq, Hkv, capacity;
   int gqa;
   int nsplit;          // splits per (b, kv head)

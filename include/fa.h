@@ -175,6 +175,32 @@ fa_status_t fa_decode(const void* q, const void* kcache, const void* vcache,
                       int B, int Hq, int Hkv, int D, int causal, float scale, int dtype,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * fa_decode_paged -- fa_decode over a paged KV cache (the decode PR page
+ * names paged KV as follow-up work beyond its identity page table).
+ *   k_pages, v_pages : [num_pages, page_size, Hkv, D] pool of pages, each
+ *               page token-major like the contiguous cache
+ *   page_table: device int32 [B, pages_per_seq]; token t of batch b is row
+ *               t % page_size of page page_table[b][t / page_size].  Read on
+ *               the device only, and only for pages holding valid tokens;
+ *               entries are clamped to [0, num_pages), so a malformed table
+ *               gives unspecified values but no access outside the pool.
+ *   valid_len : device int32[B], clamped to [0, pages_per_seq * page_size]
+ *   page_size : a multiple of 32 (a 32-token step never straddles pages)
+ *   workspace : as for fa_decode, sized by fa_decode_workspace_bytes with
+ *               capacity = pages_per_seq * page_size
+ * Limits: pages_per_seq * page_size <= 2^21 tokens and
+ * page_size * Hkv * D * 2 <= INT_MAX, else FA_ERR_SHAPE; the pool itself may
+ * exceed 2 GiB.  Other arguments, errors and semantics as fa_decode; with an
+ * identity page table over a pool that is the contiguous cache of batch 0
+ * (B = 1) the result is bitwise that of fa_decode.
+ */
+fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
+                            const int32_t* page_table, const int32_t* valid_len,
+                            int page_size, int pages_per_seq, int num_pages, void* o,
+                            int B, int Hq, int Hkv, int D, int causal, float scale, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* fa_status_string(int status);
 

@@ -29,7 +29,8 @@ to rounding order):
   token-major KV; review: the unused tail is outside the logical sequence).
 
 Packed variable-length batches (varlen_ref) apply the same definition to
-each sequence of the batch separately.
+each sequence of the batch separately; a paged decode cache
+(decode_paged_ref) is gathered into the contiguous one first.
 
 Pins: every function here is checked in tests/test_oracle_pins.py against
 brute force on tiny inputs, closed forms (identical keys -> prefix mean of V,
@@ -153,6 +154,33 @@ def decode_ref(q: np.ndarray, kcache: np.ndarray, vcache: np.ndarray, valid_len,
             allowed = np.ones((1, L), dtype=bool)
             p = probs_ref(q[b, h][None, :], kk[:, hk, :], allowed, scale)
             out[b, h] = (p @ vv[:, hk, :])[0]
+    return out
+
+
+def decode_paged_ref(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, page_table,
+                     valid_len, scale: float) -> np.ndarray:
+    """O [B, Hq, D] over a paged cache: pools [num_pages, page_size, Hkv, D]
+    and page_table [B, pages_per_seq], token t of batch b being row
+    t % page_size of page page_table[b, t // page_size] (the paged KV that the
+    decode PR page leaves as follow-up work to its identity page table).
+
+    The first L = clamp(valid_len[b], 0, pages_per_seq * page_size) tokens are
+    gathered into a contiguous cache and decode_ref's definition applied;
+    rows past L, and pages no valid token maps to, are never read."""
+    B = q.shape[0]
+    P = k_pages.shape[1]
+    page_table = np.asarray(page_table)
+    cap = P * page_table.shape[1]
+    valid_len = np.broadcast_to(np.asarray(valid_len, dtype=np.int64), (B,))
+    out = np.zeros((B, q.shape[1], v_pages.shape[3]), dtype=np.float64)
+    for b in range(B):
+        L = int(min(max(int(valid_len[b]), 0), cap))
+        if L == 0:
+            continue
+        t = np.arange(L)
+        pages, rows = page_table[b, t // P], t % P
+        kk, vv = k_pages[pages, rows], v_pages[pages, rows]  # [L, Hkv, D]
+        out[b] = decode_ref(q[b:b + 1], kk[None], vv[None], [L], scale)[0]
     return out
 
 

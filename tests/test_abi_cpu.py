@@ -30,7 +30,8 @@ def test_library_loads_and_exports_header_functions():
     lib = fa.lib()
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_lse", "fa_fwd_varlen", "fa_fwd_plan",
-                          "fa_decode_workspace_bytes", "fa_decode", "fa_status_string"}
+                          "fa_decode_workspace_bytes", "fa_decode", "fa_decode_paged",
+                          "fa_status_string"}
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES
@@ -134,6 +135,36 @@ def dec(**kw):
 ])
 def test_decode_rejects_bad_arguments(kw, code):
     assert dec(**kw) == code
+
+
+def paged(**kw):
+    a = dict(q=FAKE, kp=FAKE + 0x1000000, vp=FAKE + 0x2000000, pt=FAKE + 0x3000000,
+             vl=FAKE + 0x3000100, P=64, pps=4, npages=16, o=FAKE + 0x4000000, B=2, Hq=8, Hkv=2,
+             D=128, causal=0, scale=0.1, dtype=0, ws=FAKE + 0x5000000, wsb=None, stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        cap = max(a["P"], 1) * max(a["pps"], 1)
+        a["wsb"] = fa.decode_workspace_bytes(a["B"], a["Hq"], a["Hkv"], a["D"], cap) or 1
+    return fa.lib().fa_decode_paged(a["q"], a["kp"], a["vp"], a["pt"], a["vl"], a["P"], a["pps"],
+                                    a["npages"], a["o"], a["B"], a["Hq"], a["Hkv"], a["D"],
+                                    a["causal"], a["scale"], a["dtype"], a["ws"], a["wsb"],
+                                    a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(pt=None), NULL), (dict(kp=None), NULL), (dict(vl=None), NULL),
+    (dict(P=16), SHAPE), (dict(P=48), SHAPE), (dict(P=0), SHAPE), (dict(pps=0), SHAPE),
+    (dict(npages=0), SHAPE), (dict(P=1 << 16, pps=64), SHAPE), (dict(D=96), UNSUP),
+    (dict(pt=FAKE + 0x3000002), ALIGN), (dict(vp=FAKE + 0x2000008), ALIGN),
+    (dict(wsb=64), WS), (dict(o=FAKE + 0x3000000), ALIAS), (dict(o=FAKE + 0x1000000), ALIAS),
+    (dict(scale=float("inf")), SCALE), (dict(Hq=6, Hkv=4), SHAPE),
+])
+def test_decode_paged_rejects_bad_arguments(kw, code):
+    assert paged(**kw) == code
+
+
+def test_decode_paged_empty_batch_is_ok():
+    assert paged(B=0) == OK
 
 
 def test_decode_workspace_sizes():

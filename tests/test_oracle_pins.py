@@ -438,3 +438,47 @@ def test_unmutated_varlen_oracle_passes_its_pin():
 @pytest.mark.parametrize("mutation", VARLEN_MUTATIONS, ids=[m[1][:30] for m in VARLEN_MUTATIONS])
 def test_planted_varlen_mistake_is_caught(mutation):
     assert not _varlen_pins_pass(_mutant(*mutation))
+
+
+# ----------------------------------------------------------------------------
+# paged decode cache
+# ----------------------------------------------------------------------------
+def test_paged_decode_against_brute_force():
+    # token t of batch b: row t % P of page table[b, t // P]; every step spelled out
+    B, Hq, Hkv, D, P, pps, npages = 2, 4, 2, 3, 4, 3, 7
+    q = rnd((B, Hq, D), 151)
+    kp, vp = rnd((npages, P, Hkv, D), 152), rnd((npages, P, Hkv, D), 153)
+    table = np.array([[5, 0, 3], [2, 6, 1]])
+    L = [10, 5]
+    got = oracle.decode_paged_ref(q, kp, vp, table, L, 0.8)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // (Hq // Hkv)
+            toks = [(table[b][t // P], t % P) for t in range(L[b])]
+            s = [0.8 * sum(float(q[b, h, d]) * float(kp[pg, r, hk, d]) for d in range(D))
+                 for pg, r in toks]
+            mx = max(s)
+            w = [math.exp(x - mx) for x in s]
+            for e in range(D):
+                want = sum(wi * float(vp[pg, r, hk, e]) for wi, (pg, r) in zip(w, toks)) / sum(w)
+                assert abs(got[b, h, e] - want) < 1e-12
+
+
+def test_paged_decode_identity_and_shuffled_pools_match_contiguous():
+    B, Hq, Hkv, D, P, pps = 2, 8, 2, 16, 32, 4
+    cap = P * pps
+    q = rnd((B, Hq, D), 154)
+    kc, vc = rnd((B, cap, Hkv, D), 155), rnd((B, cap, Hkv, D), 156)
+    L = [cap - 7, 33]
+    want = oracle.decode_ref(q, kc, vc, L, 0.3)
+    # identity: batch b's pages are pool pages b*pps .. b*pps+pps-1
+    kp, vp = kc.reshape(B * pps, P, Hkv, D), vc.reshape(B * pps, P, Hkv, D)
+    ident = np.arange(B * pps).reshape(B, pps)
+    np.testing.assert_allclose(oracle.decode_paged_ref(q, kp, vp, ident, L, 0.3), want, atol=1e-12)
+    # the same pages shuffled inside a larger pool, unused pages NaN
+    perm = np.random.default_rng(157).permutation(3 * B * pps)[:B * pps]
+    kbig = np.full((3 * B * pps, P, Hkv, D), np.nan)
+    vbig = np.full((3 * B * pps, P, Hkv, D), np.nan)
+    kbig[perm], vbig[perm] = kp, vp
+    got = oracle.decode_paged_ref(q, kbig, vbig, perm.reshape(B, pps), L, 0.3)
+    np.testing.assert_allclose(got, want, atol=1e-12)
