@@ -142,55 +142,77 @@ def fwd_plan(B, Hq, Hkv, Sq, Sk, D, causal) -> dict:
     return {f: getattr(plan, f) for f, _ in FwdPlan._fields_}
 
 
-def decode_workspace_bytes(B, Hq, Hkv, D, capacity) -> int:
-    return int(lib().fa_decode_workspace_bytes(B, Hq, Hkv, D, capacity))
+def decode_workspace_bytes(B, Hq, Hkv, D, capacity, Sq: int = 1) -> int:
+    if Sq == 1:
+        return int(lib().fa_decode_workspace_bytes(B, Hq, Hkv, D, capacity))
+    return int(lib().fa_decode_multi_workspace_bytes(B, Sq, Hq, Hkv, D, capacity))
 
 
 class DecodeWorkspace:
     """Zero-filled device workspace for decode, reusable call after call on
-    one stream (each call leaves its ticket counters at zero)."""
+    one stream (each call leaves its ticket counters at zero).  Sq > 1 sizes
+    it for multi-token decode steps of Sq query tokens."""
 
-    def __init__(self, B, Hq, Hkv, D, capacity, device="cuda"):
+    def __init__(self, B, Hq, Hkv, D, capacity, device="cuda", Sq: int = 1):
         torch = _torch()
-        n = decode_workspace_bytes(B, Hq, Hkv, D, capacity)
+        n = decode_workspace_bytes(B, Hq, Hkv, D, capacity, Sq)
         if n == 0:
             raise ValueError("invalid decode sizes")
-        self.key = (B, Hq, Hkv, D, capacity)
+        self.key = (B, Sq, Hq, Hkv, D, capacity)
         self.nbytes = n
         self.buf = torch.zeros(n + 256, dtype=torch.uint8, device=device)
         off = (-self.buf.data_ptr()) % 256
         self.ptr = self.buf.data_ptr() + off
 
 
+def _q_shape(q):
+    """[B, Hq, D] (one query token) or [B, Sq, Hq, D] -> (B, Sq, Hq, D)."""
+    if q.dim() == 3:
+        return q.shape[0], 1, q.shape[1], q.shape[2]
+    if q.dim() == 4:
+        return tuple(q.shape)
+    raise ValueError("q must be [B, Hq, D] or [B, Sq, Hq, D]")
+
+
 def decode(q, kcache, vcache, valid_len, causal: bool = False, scale: float | None = None,
            out=None, workspace: DecodeWorkspace | None = None):
-    """Sq=1 attention: q [B,Hq,D] over kcache/vcache [B,capacity,Hkv,D] with
-    valid_len int32[B] on the device -> o [B,Hq,D]."""
+    """Decode attention over kcache/vcache [B,capacity,Hkv,D] with valid_len
+    int32[B] on the device.  q [B,Hq,D] -> o [B,Hq,D] (one token), or
+    q [B,Sq,Hq,D] -> o [B,Sq,Hq,D]: Sq query tokens at positions
+    L-Sq .. L-1, bottom-right causal among themselves when causal=True."""
     torch = _torch()
-    if q.dim() != 3 or kcache.dim() != 4:
-        raise ValueError("q must be [B, Hq, D] and the caches [B, capacity, Hkv, D]")
-    B, Hq, D = q.shape
+    if kcache.dim() != 4:
+        raise ValueError("the caches must be [B, capacity, Hkv, D]")
+    B, Sq, Hq, D = _q_shape(q)
     cap, Hkv = kcache.shape[1], kcache.shape[2]
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("decode needs GPU tensors")
-    _check_tensor("q", q, (B, Hq, D), q.dtype, dev)
+    _check_tensor("q", q, tuple(q.shape), q.dtype, dev)
     _check_tensor("kcache", kcache, (B, cap, Hkv, D), q.dtype, dev)
     _check_tensor("vcache", vcache, (B, cap, Hkv, D), q.dtype, dev)
     _check_tensor("valid_len", valid_len, (B,), torch.int32, dev)
     if out is None:
         out = torch.empty_like(q)
-    _check_tensor("out", out, (B, Hq, D), q.dtype, dev)
+    _check_tensor("out", out, tuple(q.shape), q.dtype, dev)
     if workspace is None:
-        workspace = DecodeWorkspace(B, Hq, Hkv, D, cap, device=dev)
-    if workspace.key != (B, Hq, Hkv, D, cap):
+        workspace = DecodeWorkspace(B, Hq, Hkv, D, cap, device=dev, Sq=Sq)
+    if workspace.key != (B, Sq, Hq, Hkv, D, cap):
         raise ValueError("workspace was sized for other shapes")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    st = lib().fa_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(), valid_len.data_ptr(),
-                         cap, out.data_ptr(), B, Hq, Hkv, D, int(bool(causal)), float(scale),
-                         _dtype_code(q), workspace.ptr, workspace.nbytes, _stream_ptr(q))
-    check(st, "fa_decode")
+    if q.dim() == 3:
+        st = lib().fa_decode(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(),
+                             valid_len.data_ptr(), cap, out.data_ptr(), B, Hq, Hkv, D,
+                             int(bool(causal)), float(scale), _dtype_code(q), workspace.ptr,
+                             workspace.nbytes, _stream_ptr(q))
+        check(st, "fa_decode")
+    else:
+        st = lib().fa_decode_multi(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(),
+                                   valid_len.data_ptr(), cap, out.data_ptr(), B, Sq, Hq, Hkv, D,
+                                   int(bool(causal)), float(scale), _dtype_code(q), workspace.ptr,
+                                   workspace.nbytes, _stream_ptr(q))
+        check(st, "fa_decode_multi")
     return out
 
 
@@ -200,36 +222,38 @@ def decode_paged(q, k_pages, v_pages, page_table, valid_len, causal: bool = Fals
     [num_pages, page_size, Hkv, D], page_table int32 [B, pages_per_seq] and
     valid_len int32[B] on the device -> o [B,Hq,D].  Token t of batch b is
     row t % page_size of page page_table[b, t // page_size]; page_size must be
-    a multiple of 32."""
+    a multiple of 32.  q [B,Sq,Hq,D] decodes Sq tokens as decode() does."""
     torch = _torch()
-    if q.dim() != 3 or k_pages.dim() != 4 or page_table.dim() != 2:
-        raise ValueError("q must be [B, Hq, D], the pools [num_pages, page_size, Hkv, D] and "
-                         "page_table [B, pages_per_seq]")
-    B, Hq, D = q.shape
+    if k_pages.dim() != 4 or page_table.dim() != 2:
+        raise ValueError("the pools must be [num_pages, page_size, Hkv, D] and page_table "
+                         "[B, pages_per_seq]")
+    B, Sq, Hq, D = _q_shape(q)
     num_pages, page_size, Hkv = k_pages.shape[0], k_pages.shape[1], k_pages.shape[2]
     pages_per_seq = page_table.shape[1]
     dev = q.device
     if dev.type != "cuda":
         raise ValueError("decode_paged needs GPU tensors")
-    _check_tensor("q", q, (B, Hq, D), q.dtype, dev)
+    _check_tensor("q", q, tuple(q.shape), q.dtype, dev)
     _check_tensor("k_pages", k_pages, (num_pages, page_size, Hkv, D), q.dtype, dev)
     _check_tensor("v_pages", v_pages, (num_pages, page_size, Hkv, D), q.dtype, dev)
     _check_tensor("page_table", page_table, (B, pages_per_seq), torch.int32, dev)
     _check_tensor("valid_len", valid_len, (B,), torch.int32, dev)
     if out is None:
         out = torch.empty_like(q)
-    _check_tensor("out", out, (B, Hq, D), q.dtype, dev)
+    _check_tensor("out", out, tuple(q.shape), q.dtype, dev)
     cap = pages_per_seq * page_size
     if workspace is None:
-        workspace = DecodeWorkspace(B, Hq, Hkv, D, cap, device=dev)
-    if workspace.key != (B, Hq, Hkv, D, cap):
+        workspace = DecodeWorkspace(B, Hq, Hkv, D, cap, device=dev, Sq=Sq)
+    if workspace.key != (B, Sq, Hq, Hkv, D, cap):
         raise ValueError("workspace was sized for other shapes")
     if scale is None:
         scale = 1.0 / math.sqrt(D)
-    st = lib().fa_decode_paged(q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(),
-                               page_table.data_ptr(), valid_len.data_ptr(), page_size,
-                               pages_per_seq, num_pages, out.data_ptr(), B, Hq, Hkv, D,
-                               int(bool(causal)), float(scale), _dtype_code(q), workspace.ptr,
-                               workspace.nbytes, _stream_ptr(q))
-    check(st, "fa_decode_paged")
+    args = (q.data_ptr(), k_pages.data_ptr(), v_pages.data_ptr(), page_table.data_ptr(),
+            valid_len.data_ptr(), page_size, pages_per_seq, num_pages, out.data_ptr(), B)
+    tail = (Hq, Hkv, D, int(bool(causal)), float(scale), _dtype_code(q), workspace.ptr,
+            workspace.nbytes, _stream_ptr(q))
+    if q.dim() == 3:
+        check(lib().fa_decode_paged(*args, *tail), "fa_decode_paged")
+    else:
+        check(lib().fa_decode_paged_multi(*args, Sq, *tail), "fa_decode_paged_multi")
     return out

@@ -241,20 +241,22 @@ fa_status_t launch_varlen(const void* q, const void* k, const void* v, void* o, 
 // Sq = 1 decode over a contiguous cache (page_table == nullptr) or a paged
 // pool; all checks before any HIP call.
 constexpr long long kMaxPagedCapacity = 1LL << 21;  // tokens a paged sequence may span
+constexpr int kMaxDecodeSq = 32;                    // query tokens of one decode step
 
 fa_status_t decode_impl(const void* q, const void* kc, const void* vc, const int32_t* valid_len,
                         const int32_t* page_table, int page_size, int pages_per_seq,
-                        int num_pages, int capacity, void* o, int B, int Hq, int Hkv, int D,
-                        float scale, int dtype, void* workspace, size_t workspace_bytes,
-                        void* stream) {
+                        int num_pages, int capacity, void* o, int B, int Sq, int Hq, int Hkv,
+                        int D, int causal, float scale, int dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
   const bool paged = page_size > 0;
   if (B < 0 || Hq < 1 || Hkv < 1 || capacity < 1) return FA_ERR_SHAPE;
+  if (Sq < 1 || Sq > kMaxDecodeSq) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
   if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
   long long nq, ncache, ntable = 0;
-  if (!count4(B, Hq, D, 1, &nq)) return FA_ERR_SHAPE;
+  if (!count4(B, Sq, Hq, D, &nq)) return FA_ERR_SHAPE;
   if (paged) {
     if (!count4(num_pages, page_size, Hkv, D, &ncache) || !count4(B, pages_per_seq, 1, 1, &ntable))
       return FA_ERR_SHAPE;
@@ -273,7 +275,8 @@ fa_status_t decode_impl(const void* q, const void* kc, const void* vc, const int
     if (!aligned16(ptr)) return FA_ERR_ALIGN;
   if ((reinterpret_cast<uintptr_t>(valid_len) & 3u) != 0) return FA_ERR_ALIGN;
   if (paged && (reinterpret_cast<uintptr_t>(page_table) & 3u) != 0) return FA_ERR_ALIGN;
-  const size_t need = fa::decode_workspace_layout(B, Hq, Hkv, D, capacity, nullptr, nullptr);
+  const size_t need =
+      fa::decode_workspace_layout(B, Sq, Hq, Hkv, D, capacity, nullptr, nullptr);
   if (!workspace || workspace_bytes < need ||
       (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
     return FA_ERR_WORKSPACE;
@@ -290,7 +293,7 @@ fa_status_t decode_impl(const void* q, const void* kc, const void* vc, const int
   p.valid_len = valid_len;
   p.o = o;
   size_t off_ml = 0, off_tickets = 0;
-  fa::decode_workspace_layout(B, Hq, Hkv, D, capacity, &off_ml, &off_tickets);
+  fa::decode_workspace_layout(B, Sq, Hq, Hkv, D, capacity, &off_ml, &off_tickets);
   char* ws = static_cast<char*>(workspace);
   p.part_o = reinterpret_cast<float*>(ws);
   p.part_ml = reinterpret_cast<float*>(ws + off_ml);
@@ -300,6 +303,9 @@ fa_status_t decode_impl(const void* q, const void* kc, const void* vc, const int
   p.pages_per_seq = pages_per_seq;
   p.num_pages = num_pages;
   p.gqa = Hq / Hkv;
+  p.sq = Sq;
+  p.hpg = fa::decode_heads_per_group(p.gqa, Sq);
+  p.causal = causal ? 1 : 0;
   p.nsplit = fa::decode_num_splits(B, Hkv, capacity);
   p.B = B;
   p.Hq = Hq;
@@ -308,6 +314,20 @@ fa_status_t decode_impl(const void* q, const void* kc, const void* vc, const int
   fold_scale(scale, &p.c_log2, &p.q_sign);
   const hipError_t e = fa::launch_decode(p, D, dtype, static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
+fa_status_t paged_impl(const void* q, const void* k_pages, const void* v_pages,
+                       const int32_t* page_table, const int32_t* valid_len, int page_size,
+                       int pages_per_seq, int num_pages, void* o, int B, int Sq, int Hq, int Hkv,
+                       int D, int causal, float scale, int dtype, void* workspace,
+                       size_t workspace_bytes, void* stream) {
+  if (page_size < 32 || page_size % 32 != 0 || pages_per_seq < 1 || num_pages < 1)
+    return FA_ERR_SHAPE;
+  const long long capacity = (long long)pages_per_seq * page_size;
+  if (capacity > kMaxPagedCapacity) return FA_ERR_SHAPE;
+  return decode_impl(q, k_pages, v_pages, valid_len, page_table, page_size, pages_per_seq,
+                     num_pages, (int)capacity, o, B, Sq, Hq, Hkv, D, causal, scale, dtype,
+                     workspace, workspace_bytes, stream);
 }
 
 }  // namespace
@@ -345,16 +365,31 @@ fa_status_t fa_fwd_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causa
 
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int capacity) {
   if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv || (D != 64 && D != 128) || capacity < 1) return 0;
-  return fa::decode_workspace_layout(B, Hq, Hkv, D, capacity, nullptr, nullptr);
+  return fa::decode_workspace_layout(B, 1, Hq, Hkv, D, capacity, nullptr, nullptr);
+}
+
+size_t fa_decode_multi_workspace_bytes(int B, int Sq, int Hq, int Hkv, int D, int capacity) {
+  if (B < 0 || Sq < 1 || Sq > kMaxDecodeSq || Hq < 1 || Hkv < 1 || Hq % Hkv ||
+      (D != 64 && D != 128) || capacity < 1)
+    return 0;
+  return fa::decode_workspace_layout(B, Sq, Hq, Hkv, D, capacity, nullptr, nullptr);
 }
 
 fa_status_t fa_decode(const void* q, const void* kcache, const void* vcache,
                       const int32_t* valid_len, int capacity, void* o, int B, int Hq, int Hkv,
                       int D, int causal, float scale, int dtype, void* workspace,
                       size_t workspace_bytes, void* stream) {
-  (void)causal;  // at Sq = 1 the bottom-right causal mask admits every valid token
-  return decode_impl(q, kcache, vcache, valid_len, nullptr, 0, 0, 0, capacity, o, B, Hq, Hkv, D,
-                     scale, dtype, workspace, workspace_bytes, stream);
+  // at Sq = 1 the bottom-right causal mask admits every valid token
+  return decode_impl(q, kcache, vcache, valid_len, nullptr, 0, 0, 0, capacity, o, B, 1, Hq, Hkv,
+                     D, causal, scale, dtype, workspace, workspace_bytes, stream);
+}
+
+fa_status_t fa_decode_multi(const void* q, const void* kcache, const void* vcache,
+                            const int32_t* valid_len, int capacity, void* o, int B, int Sq,
+                            int Hq, int Hkv, int D, int causal, float scale, int dtype,
+                            void* workspace, size_t workspace_bytes, void* stream) {
+  return decode_impl(q, kcache, vcache, valid_len, nullptr, 0, 0, 0, capacity, o, B, Sq, Hq, Hkv,
+                     D, causal, scale, dtype, workspace, workspace_bytes, stream);
 }
 
 fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pages,
@@ -362,14 +397,20 @@ fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pa
                             int pages_per_seq, int num_pages, void* o, int B, int Hq, int Hkv,
                             int D, int causal, float scale, int dtype, void* workspace,
                             size_t workspace_bytes, void* stream) {
-  (void)causal;
-  if (page_size < 32 || page_size % 32 != 0 || pages_per_seq < 1 || num_pages < 1)
-    return FA_ERR_SHAPE;
-  const long long capacity = (long long)pages_per_seq * page_size;
-  if (capacity > kMaxPagedCapacity) return FA_ERR_SHAPE;
-  return decode_impl(q, k_pages, v_pages, valid_len, page_table, page_size, pages_per_seq,
-                     num_pages, (int)capacity, o, B, Hq, Hkv, D, scale, dtype, workspace,
-                     workspace_bytes, stream);
+  return paged_impl(q, k_pages, v_pages, page_table, valid_len, page_size, pages_per_seq,
+                    num_pages, o, B, 1, Hq, Hkv, D, causal, scale, dtype, workspace,
+                    workspace_bytes, stream);
+}
+
+fa_status_t fa_decode_paged_multi(const void* q, const void* k_pages, const void* v_pages,
+                                  const int32_t* page_table, const int32_t* valid_len,
+                                  int page_size, int pages_per_seq, int num_pages, void* o, int B,
+                                  int Sq, int Hq, int Hkv, int D, int causal, float scale,
+                                  int dtype, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  return paged_impl(q, k_pages, v_pages, page_table, valid_len, page_size, pages_per_seq,
+                    num_pages, o, B, Sq, Hq, Hkv, D, causal, scale, dtype, workspace,
+                    workspace_bytes, stream);
 }
 
 const char* fa_status_string(int status) {

@@ -44,7 +44,10 @@ constexpr int kMergeGroup = 16;  // partials merged by one workgroup
 constexpr bool kMergeKernel = FA_DECODE_MERGE_KERNEL != 0;
 constexpr int kDVPad = 32;       // V staging row pad (elements)
 
-__device__ __forceinline__ int heads_in_group(int gqa, int hg) { return min(32, gqa - 32 * hg); }
+// Query heads of head group hg (groups of hpg heads of one kv head's gqa).
+__device__ __forceinline__ int heads_in_group(int hpg, int gqa, int hg) {
+  return min(hpg, gqa - hpg * hg);
+}
 
 // Partials cross workgroups (and XCDs, whose L2 caches are not coherent with
 // each other) through loads and stores with the sc1 cache policy (what an
@@ -94,12 +97,14 @@ __device__ __forceinline__ void st2_coherent(__amdgpu_buffer_rsrc_t rs, int off,
 // Merge records [first, first + n) (n <= kMergeGroup) of one unit's partials
 // in global memory -- o records of gg x D floats at byte 0 of `ro`, (m, l)
 // pairs at byte 0 of `rml` -- into record `dst` of the same unit, or, when
-// `out` is not null, normalise and write O.  Every thread issues all of its
+// `out` is not null, normalise and write O.  Column g of a record is query
+// token g / gh, head g % gh of the group; its O row starts at
+// out + out_base + (g / gh) * ostride + (g % gh) * D.  Every thread issues all of its
 // record loads before using any, so a merge costs about one memory round trip.
 template <int D, int DT>
 __device__ void merge_global(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rml, int first,
-                             int n, int gg, int dst, uint16_t* out, long long out_base,
-                             float* lds_scratch) {
+                             int n, int gg, int cs, int dst, uint16_t* out, long long out_base,
+                             int gh, long long ostride, float* lds_scratch) {
   using E = Elt<DT>;
   constexpr int Q = D / 4;              // 16-byte pieces per head row
   float* w = lds_scratch;               // [gg][kMergeGroup] weights 2^(m_s - M)
@@ -109,7 +114,7 @@ __device__ void merge_global(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t r
     f32x2 ml[kMergeGroup];
 #pragma unroll
     for (int s = 0; s < kMergeGroup; ++s)
-      if (s < n) ml[s] = ld2_coherent(rml, ((first + s) * gg + g) * 8);
+      if (s < n) ml[s] = ld2_coherent(rml, ((first + s) * cs + g) * 8);
     float M = -__builtin_inff();
 #pragma unroll
     for (int s = 0; s < kMergeGroup; ++s)
@@ -133,7 +138,7 @@ __device__ void merge_global(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t r
     f32x4 x[kMergeGroup];
 #pragma unroll
     for (int s = 0; s < kMergeGroup; ++s)
-      if (s < n) x[s] = ld4_coherent(ro, (((first + s) * gg + g) * D + 4 * q) * 4);
+      if (s < n) x[s] = ld4_coherent(ro, (((first + s) * cs + g) * D + 4 * q) * 4);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int s = 0; s < kMergeGroup; ++s) {
@@ -146,26 +151,29 @@ __device__ void merge_global(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t r
       const float dd = den[g];
       const float inv = dd > 0.f ? 1.0f / dd : 0.f;
       const u32x2 pk = {E::pack2(acc[0] * inv, acc[1] * inv), E::pack2(acc[2] * inv, acc[3] * inv)};
-      *reinterpret_cast<u32x2*>(out + out_base + (long long)g * D + 4 * q) = pk;
+      *reinterpret_cast<u32x2*>(out + out_base + (long long)(g / gh) * ostride +
+                                (long long)(g % gh) * D + 4 * q) = pk;
     } else {
-      st4_coherent(ro, ((dst * gg + g) * D + 4 * q) * 4, acc);
+      st4_coherent(ro, ((dst * cs + g) * D + 4 * q) * 4, acc);
     }
   }
   if (!out) {
     for (int g = threadIdx.x; g < gg; g += blockDim.x)
-      st2_coherent(rml, (dst * gg + g) * 8, f32x2{Mh[g], den[g]});
+      st2_coherent(rml, (dst * cs + g) * 8, f32x2{Mh[g], den[g]});
   }
   __syncthreads();
 }
 
-// Merge the workgroup's `n` wave records (o: [n][gg][D], ml: [n][gg][2], in
-// LDS) into record `dst` of the unit's partials in global memory (written
-// coherently, 16 bytes at a time), or, when `out` is not null, normalise and
-// write O.
+// Merge the workgroup's `n` wave records (o: [n][cs][D], ml: [n][cs][2], in
+// LDS; columns g < gg in use) into record `dst` of the unit's partials in
+// global memory (records of cs columns, written coherently, 16 bytes at a
+// time), or, when `out` is not null, normalise and write O as merge_global
+// does.
 template <int D, int DT>
-__device__ void merge_waves(const float* src_o, const float* src_ml, int n, int gg,
+__device__ void merge_waves(const float* src_o, const float* src_ml, int n, int gg, int cs,
                             __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rml, int dst,
-                            uint16_t* out, long long out_base, float* lds_scratch) {
+                            uint16_t* out, long long out_base, int gh, long long ostride,
+                            float* lds_scratch) {
   using E = Elt<DT>;
   constexpr int Q = D / 4;
   float* w = lds_scratch;              // [gg][n] weights 2^(m_s - M)
@@ -173,13 +181,13 @@ __device__ void merge_waves(const float* src_o, const float* src_ml, int n, int 
   float* Mh = den + gg;                // [gg]
   for (int g = threadIdx.x; g < gg; g += blockDim.x) {
     float M = -__builtin_inff();
-    for (int s = 0; s < n; ++s) M = fmaxf(M, src_ml[(s * gg + g) * 2]);
+    for (int s = 0; s < n; ++s) M = fmaxf(M, src_ml[(s * cs + g) * 2]);
     const float Mu = (M == -__builtin_inff()) ? 0.f : M;
     float dsum = 0.f;
     for (int s = 0; s < n; ++s) {
-      const float f = fast_exp2(src_ml[(s * gg + g) * 2] - Mu);  // m = -inf -> 0
+      const float f = fast_exp2(src_ml[(s * cs + g) * 2] - Mu);  // m = -inf -> 0
       w[g * n + s] = f;
-      dsum += f * src_ml[(s * gg + g) * 2 + 1];
+      dsum += f * src_ml[(s * cs + g) * 2 + 1];
     }
     den[g] = dsum;
     Mh[g] = M;
@@ -190,21 +198,22 @@ __device__ void merge_waves(const float* src_o, const float* src_ml, int n, int 
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     for (int s = 0; s < n; ++s) {
       const float f = w[g * n + s];
-      const f32x4 x = *reinterpret_cast<const f32x4*>(src_o + (s * gg + g) * D + 4 * q);
+      const f32x4 x = *reinterpret_cast<const f32x4*>(src_o + (s * cs + g) * D + 4 * q);
       if (f != 0.f) acc += f * x;
     }
     if (out) {
       const float dd = den[g];
       const float inv = dd > 0.f ? 1.0f / dd : 0.f;
       const u32x2 pk = {E::pack2(acc[0] * inv, acc[1] * inv), E::pack2(acc[2] * inv, acc[3] * inv)};
-      *reinterpret_cast<u32x2*>(out + out_base + (long long)g * D + 4 * q) = pk;
+      *reinterpret_cast<u32x2*>(out + out_base + (long long)(g / gh) * ostride +
+                                (long long)(g % gh) * D + 4 * q) = pk;
     } else {
-      st4_coherent(ro, ((dst * gg + g) * D + 4 * q) * 4, acc);
+      st4_coherent(ro, ((dst * cs + g) * D + 4 * q) * 4, acc);
     }
   }
   if (!out) {
     for (int g = threadIdx.x; g < gg; g += blockDim.x)
-      st2_coherent(rml, (dst * gg + g) * 8, f32x2{Mh[g], den[g]});
+      st2_coherent(rml, (dst * cs + g) * 8, f32x2{Mh[g], den[g]});
   }
   __syncthreads();
 }
@@ -243,13 +252,17 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   // grid: x = split, y = unit (b, kv head, head group)
   const int split = blockIdx.x;
   const int unit = blockIdx.y;
-  const int HG = (p.gqa + 31) / 32;
+  // a unit's MFMA columns are (query token t, head g of the group): column
+  // t * gh + g for t < sq, g < gh, at most 32 of them
+  const int HG = (p.gqa + p.hpg - 1) / p.hpg;
   const int hg = unit % HG;
   const int bk = unit / HG;
   const int b = bk / p.Hkv;
   const int hk = bk - b * p.Hkv;
-  const int gg = heads_in_group(p.gqa, hg);
-  const int hq0 = hk * p.gqa + 32 * hg;  // first query head of this group
+  const int gh = heads_in_group(p.hpg, p.gqa, hg);
+  const int gg = gh * p.sq;                        // columns in use
+  const int cstride = min(p.hpg, p.gqa) * p.sq;   // columns per record
+  const int hq0 = hk * p.gqa + p.hpg * hg;  // first query head of this group
 
   int L = p.valid_len[b];
   L = min(max(L, 0), p.capacity);
@@ -286,7 +299,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
     u32x4 x = {0u, 0u, 0u, 0u};
-    if (li < gg) x = gload16(qg + ((long long)b * p.Hq + hq0 + li) * D + 16 * kk + 8 * lh);
+    if (li < gg) {
+      const int t = li / gh;
+      x = gload16(qg + (((long long)b * p.sq + t) * p.Hq + hq0 + li - t * gh) * D + 16 * kk + 8 * lh);
+    }
     if (p.q_sign < 0) x ^= 0x80008000u;
     if (p.q_sign == 0) x = u32x4{0u, 0u, 0u, 0u};
     qr[kk] = x;
@@ -318,6 +334,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   const int v_lane = (4 * lh + (ti >> 2)) * VST + 16 * ((lane >> 4) & 1) + 4 * (ti & 3);
   // K rows (A operand): lane row li, d = 16kk + 8lh
   const unsigned k_off = (unsigned)((li * tok_stride + 8 * lh) * 2);
+
+  // Query token t of the sq sits at position L - sq + t: with the causal
+  // mask (bottom-right) it sees keys j <= L - sq + t, else every j < L.
+  // key_lim is the last key this lane's column sees, mask_from the first key
+  // that some column does not see.
+  const int key_lim = p.causal ? L - p.sq + (li < gg ? li / gh : 0) : L - 1;
+  const int mask_from = p.causal ? L - p.sq + 1 : L;
 
   f32x16 oacc[DTILES];
 #pragma unroll
@@ -353,12 +376,13 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     f32x16 s = f32x16{};
 #pragma unroll
     for (int kk = 0; kk < KSTEPS; ++kk) s = E::mfma(kr[kk], qr[kk], s);
-    // scores of tokens >= L are excluded (their K rows were zero, not -inf)
-    if (tok0 + 32 > L) {
+    // scores of keys a column does not see are excluded (keys >= L had zero
+    // K rows, not -inf)
+    if (tok0 + 32 > mask_from) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int j = tok0 + 8 * (r >> 2) + 4 * lh + (r & 3);
-        if (j >= L) s[r] = -__builtin_inff();
+        if (j > key_lim) s[r] = -__builtin_inff();
       }
     }
     float mx = s[0];
@@ -444,8 +468,10 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
 
   // ---- merge the waves of this workgroup (through LDS) -> split partial ----
   __syncthreads();  // V staging no longer needed; reuse dyn_lds
-  float* wo = reinterpret_cast<float*>(dyn_lds);      // [NW][gg][D]
-  float* wml = wo + NW * gg * D;                       // [NW][gg][2]
+  // wave records in LDS and global records alike hold cstride columns, of
+  // which the first gg are in use: [NW][cstride][D] and [NW][cstride][2]
+  float* wo = reinterpret_cast<float*>(dyn_lds);
+  float* wml = wo + NW * cstride * D;
   const float l_tot = pair_sum(l_run);
   if (li < gg) {
 #pragma unroll
@@ -453,30 +479,32 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int d = 32 * dt + 8 * (r >> 2) + 4 * lh + (r & 3);
-        wo[(wave * gg + li) * D + d] = oacc[dt][r];
+        wo[(wave * cstride + li) * D + d] = oacc[dt][r];
       }
     if (lh == 0) {
-      wml[(wave * gg + li) * 2 + 0] = m_run;
-      wml[(wave * gg + li) * 2 + 1] = l_tot;
+      wml[(wave * cstride + li) * 2 + 0] = m_run;
+      wml[(wave * cstride + li) * 2 + 1] = l_tot;
     }
   }
   __syncthreads();
-  float* scratch = wml + NW * gg * 2;  // merge weights and per-head sums
+  float* scratch = wml + NW * cstride * 2;  // merge weights and per-column sums
   const int ngroups = (p.nsplit + kMergeGroup - 1) / kMergeGroup;
   const int nrec = p.nsplit + ngroups;  // level-0 records, then level-1 records
   const long long unit_parts = (long long)unit * nrec;
   const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
-      p.part_o + unit_parts * gg * D, (short)0, nrec * gg * D * 4, kBufferFlags);
+      p.part_o + unit_parts * cstride * D, (short)0, nrec * cstride * D * 4, kBufferFlags);
   const __amdgpu_buffer_rsrc_t rml = __builtin_amdgcn_make_buffer_rsrc(
-      p.part_ml + unit_parts * gg * 2, (short)0, nrec * gg * 2 * 4, kBufferFlags);
+      p.part_ml + unit_parts * cstride * 2, (short)0, nrec * cstride * 2 * 4, kBufferFlags);
   uint16_t* og = static_cast<uint16_t*>(p.o);
-  const long long out_base = ((long long)b * p.Hq + hq0) * D;
+  // O is [B, sq, Hq, D]: column (t, g) -> row (b, t, hq0 + g)
+  const long long out_base = ((long long)b * p.sq * p.Hq + hq0) * D;
+  const long long ostride = (long long)p.Hq * D;
 
   if (p.nsplit == 1) {
-    merge_waves<D, DT>(wo, wml, NW, gg, ro, rml, 0, og, out_base, scratch);
+    merge_waves<D, DT>(wo, wml, NW, gg, cstride, ro, rml, 0, og, out_base, gh, ostride, scratch);
     return;
   }
-  merge_waves<D, DT>(wo, wml, NW, gg, ro, rml, split, nullptr, 0, scratch);
+  merge_waves<D, DT>(wo, wml, NW, gg, cstride, ro, rml, split, nullptr, 0, gh, ostride, scratch);
   if (kMergeKernel) return;  // the split records are merged by decode_merge_kernel
 
   // ---- level 1: last workgroup of the group merges the group -------------------
@@ -490,17 +518,19 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   int* ticket_flag = reinterpret_cast<int*>(dyn_lds + p.lds_bytes) - 1;
   if (!take_ticket(cnt0 + grp, (unsigned)gsize, ticket_flag)) return;
   if (ngroups == 1) {
-    merge_global<D, DT>(ro, rml, gfirst, gsize, gg, 0, og, out_base, scratch);
+    merge_global<D, DT>(ro, rml, gfirst, gsize, gg, cstride, 0, og, out_base, gh, ostride, scratch);
     return;
   }
-  merge_global<D, DT>(ro, rml, gfirst, gsize, gg, p.nsplit + grp, nullptr, 0, scratch);
+  merge_global<D, DT>(ro, rml, gfirst, gsize, gg, cstride, p.nsplit + grp, nullptr, 0, gh, ostride,
+                      scratch);
   // ---- level 2: last group merger merges the groups and writes O -----------
   if (!take_ticket(cnt0 + ngroups, (unsigned)ngroups, ticket_flag)) return;
-  merge_global<D, DT>(ro, rml, p.nsplit, ngroups, gg, 0, og, out_base, scratch);
+  merge_global<D, DT>(ro, rml, p.nsplit, ngroups, gg, cstride, 0, og, out_base, gh, ostride, scratch);
 }
 
 // Second kernel: merges the nsplit (<= 256, see decode_num_splits) split
-// records of (unit, head g of the group) for 32 columns of O.  Thread t takes
+// records of (unit, column g = (query token, head) of the group) for 32
+// columns of O.  Thread t takes
 // columns 4 (t % 8) .. + 3 of records s = t / 8 + 32 k.  The kernel boundary
 // makes the records visible, so plain loads suffice; they do not depend on
 // the merge weights, so they are issued first, together with the (m, l)
@@ -513,29 +543,30 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
   __shared__ float w[256];
   __shared__ float red[NW][2];
   __shared__ f32x4 part[NW][8];
-  const int unit = blockIdx.x, g = blockIdx.y, col0 = 32 * blockIdx.z;
-  const int HG = (p.gqa + 31) / 32;
+  const int unit = blockIdx.x, g = blockIdx.y, col0 = 32 * blockIdx.z;  // g: record column
+  const int HG = (p.gqa + p.hpg - 1) / p.hpg;
   const int hg = unit % HG;
   const int bk = unit / HG;
   const int b = bk / p.Hkv, hk = bk - b * p.Hkv;
-  const int gg = heads_in_group(p.gqa, hg);
-  if (g >= gg) return;
+  const int gh = heads_in_group(p.hpg, p.gqa, hg);
+  const int cs = min(p.hpg, p.gqa) * p.sq;  // columns per record
+  if (g >= gh * p.sq) return;
   const int ns = p.nsplit;
   const int ngroups = (ns + kMergeGroup - 1) / kMergeGroup;
   const long long rec0 = (long long)unit * (ns + ngroups);  // this unit's first record
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int cg = t & 7, rl = t >> 3;
-  const float* po = p.part_o + (rec0 * gg + g) * D + col0 + 4 * cg;
+  const float* po = p.part_o + (rec0 * cs + g) * D + col0 + 4 * cg;
   f32x4 x[8];
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int s = rl + 32 * k;
-    x[k] = s < ns ? *reinterpret_cast<const f32x4*>(po + (long long)s * gg * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+    x[k] = s < ns ? *reinterpret_cast<const f32x4*>(po + (long long)s * cs * D) : f32x4{0.f, 0.f, 0.f, 0.f};
   }
   // weights: M = max_s m_s, w_s = 2^(m_s - M), den = sum_s w_s l_s
   float m = -__builtin_inff(), l = 0.f;
   if (t < ns) {
-    const f32x2 ml = *reinterpret_cast<const f32x2*>(p.part_ml + ((rec0 + t) * gg + g) * 2);
+    const f32x2 ml = *reinterpret_cast<const f32x2*>(p.part_ml + ((rec0 + t) * cs + g) * 2);
     m = ml[0];
     l = ml[1];
   }
@@ -580,15 +611,16 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
     const float inv = den > 0.f ? 1.0f / den : 0.f;
     const u32x2 pk = {E::pack2(sum[0] * inv, sum[1] * inv), E::pack2(sum[2] * inv, sum[3] * inv)};
     uint16_t* og = static_cast<uint16_t*>(p.o);
-    const int hq = hk * p.gqa + 32 * hg + g;
-    *reinterpret_cast<u32x2*>(og + ((long long)b * p.Hq + hq) * D + col0 + 4 * t) = pk;
+    const int qt = g / gh;                              // query token of the column
+    const int hq = hk * p.gqa + p.hpg * hg + g - qt * gh;
+    *reinterpret_cast<u32x2*>(og + (((long long)b * p.sq + qt) * p.Hq + hq) * D + col0 + 4 * t) = pk;
   }
 }
 
 template <int D, int DT, bool PAGED>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
-  const int HG = (p.gqa + 31) / 32;
-  const int gg = min(32, p.gqa);
+  const int HG = (p.gqa + p.hpg - 1) / p.hpg;
+  const int gg = min(p.hpg, p.gqa) * p.sq;  // columns per record
   const int ngroups = (p.nsplit + kMergeGroup - 1) / kMergeGroup;
   const size_t stage = (size_t)kDecodeWaves * 2 * 32 * (D + kDVPad) * 2;
   int nmax = kDecodeWaves;  // most records any merge step reads
@@ -629,11 +661,17 @@ int decode_num_splits(int B, int Hkv, int capacity) {
   return ns;
 }
 
-size_t decode_workspace_layout(int B, int Hq, int Hkv, int D, int capacity, size_t* off_ml,
-                               size_t* off_tickets) {
+int decode_heads_per_group(int gqa, int sq) {
+  const int h = 32 / sq;
+  return gqa < h ? gqa : h;
+}
+
+size_t decode_workspace_layout(int B, int Sq, int Hq, int Hkv, int D, int capacity,
+                               size_t* off_ml, size_t* off_tickets) {
   const int gqa = Hq / Hkv;
-  const int HG = (gqa + 31) / 32;
-  const int gg = gqa < 32 ? gqa : 32;
+  const int hpg = decode_heads_per_group(gqa, Sq);
+  const int HG = (gqa + hpg - 1) / hpg;
+  const int gg = hpg * Sq;  // columns per record
   const int ns = decode_num_splits(B, Hkv, capacity);
   const int ngroups = (ns + kMergeGroup - 1) / kMergeGroup;
   const size_t units = (size_t)B * Hkv * HG;

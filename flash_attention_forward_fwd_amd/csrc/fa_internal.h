@@ -73,6 +73,9 @@ struct DecodeParams {
   int page_size, pages_per_seq, num_pages;
   int B, Hq, Hkv, capacity;
   int gqa;
+  int sq;              // query tokens per sequence (1 = plain decode), <= 32
+  int hpg;             // query heads per head group: min(gqa, 32 / sq)
+  int causal;          // bottom-right mask among the sq query tokens
   int nsplit;          // splits per (b, kv head)
   int lds_bytes;       // dynamic LDS of the launch (set by the launcher)
   float c_log2;
@@ -80,10 +83,11 @@ struct DecodeParams {
 };
 
 int decode_num_splits(int B, int Hkv, int capacity);
+int decode_heads_per_group(int gqa, int sq);
 // Workspace layout: part_o at offset 0, part_ml at *off_ml, tickets at
 // *off_tickets (either pointer may be null); returns the total size.
-size_t decode_workspace_layout(int B, int Hq, int Hkv, int D, int capacity, size_t* off_ml,
-                               size_t* off_tickets);
+size_t decode_workspace_layout(int B, int Sq, int Hq, int Hkv, int D, int capacity,
+                               size_t* off_ml, size_t* off_tickets);
 hipError_t launch_decode(const DecodeParams& p, int D, int dtype, hipStream_t stream);
 
 }  // namespace fa

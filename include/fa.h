@@ -201,6 +201,36 @@ fa_status_t fa_decode_paged(const void* q, const void* k_pages, const void* v_pa
                             int B, int Hq, int Hkv, int D, int causal, float scale, int dtype,
                             void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * Multi-token (speculative) decode: Sq query tokens per sequence in one call
+ * (the decode PR page leaves Sq > 1 decode as follow-up work).
+ *   q, o : [B, Sq, Hq, D]; query token t of batch b sits at position
+ *          L - Sq + t of its sequence (L = clamp(valid_len[b], 0, capacity)),
+ *          i.e. the tokens being decoded are the last Sq valid ones.
+ *   causal != 0: token t sees keys j <= L - Sq + t (bottom-right causal, the
+ *          prefill mask with Sk = L); causal == 0: every j < L.  A token with
+ *          no key to see (L - Sq + t < 0) gets O = 0.
+ *   1 <= Sq <= 32.  Sq = 1 is fa_decode / fa_decode_paged exactly.
+ *   workspace : at least fa_decode_multi_workspace_bytes(B, Sq, Hq, Hkv, D,
+ *          capacity) bytes (capacity = pages_per_seq * page_size if paged),
+ *          otherwise as for fa_decode.
+ * The other arguments, limits and errors are those of fa_decode and
+ * fa_decode_paged.
+ */
+size_t fa_decode_multi_workspace_bytes(int B, int Sq, int Hq, int Hkv, int D, int capacity);
+
+fa_status_t fa_decode_multi(const void* q, const void* kcache, const void* vcache,
+                            const int32_t* valid_len, int capacity, void* o,
+                            int B, int Sq, int Hq, int Hkv, int D, int causal, float scale,
+                            int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
+fa_status_t fa_decode_paged_multi(const void* q, const void* k_pages, const void* v_pages,
+                                  const int32_t* page_table, const int32_t* valid_len,
+                                  int page_size, int pages_per_seq, int num_pages, void* o,
+                                  int B, int Sq, int Hq, int Hkv, int D, int causal,
+                                  float scale, int dtype, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* fa_status_string(int status);
 

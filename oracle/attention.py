@@ -83,7 +83,7 @@ def probs_ref(q_rows: np.ndarray, k: np.ndarray, allowed: np.ndarray, scale: flo
     Rows with no admissible key are all zero."""
     s = scale * (q_rows @ k.T)
     s = np.where(allowed, s, -np.inf)
-    m = s.max(axis=1, keepdims=True)
+    m = np.max(s, axis=1, keepdims=True, initial=-np.inf)  # also for Sk = 0
     empty = ~allowed.any(axis=1, keepdims=True)
     m = np.where(empty, 0.0, m)
     w = np.where(allowed, np.exp(s - m), 0.0)
@@ -157,30 +157,55 @@ def decode_ref(q: np.ndarray, kcache: np.ndarray, vcache: np.ndarray, valid_len,
     return out
 
 
+def decode_multi_ref(q: np.ndarray, kcache: np.ndarray, vcache: np.ndarray, valid_len,
+                     causal: bool, scale: float) -> np.ndarray:
+    """O [B, Sq, Hq, D] for Sq query tokens per sequence, q [B, Sq, Hq, D],
+    over kcache, vcache [B, capacity, Hkv, D] (multi-token decode, named as
+    follow-up work on the decode PR page).
+
+    Query token t sits at position L - Sq + t of its sequence, so with the
+    bottom-right causal mask it sees keys j <= L - Sq + t: this is the
+    definition above with Sq queries against Sk = L keys (only the first L
+    cache rows are read).  Without the mask every token sees all L keys."""
+    B, Sq, Hq, _ = q.shape
+    cap = kcache.shape[1]
+    valid_len = np.broadcast_to(np.asarray(valid_len, dtype=np.int64), (B,))
+    out = np.zeros((B, Sq, Hq, vcache.shape[3]), dtype=np.float64)
+    for b in range(B):
+        L = int(min(max(int(valid_len[b]), 0), cap))
+        qs = q[b].transpose(1, 0, 2)[None]           # [1, Hq, Sq, D]
+        ks = kcache[b, :L].transpose(1, 0, 2)[None]  # [1, Hkv, L, D]
+        vs = vcache[b, :L].transpose(1, 0, 2)[None]
+        out[b] = attention_ref(qs, ks, vs, causal, scale)[0].transpose(1, 0, 2)
+    return out
+
+
 def decode_paged_ref(q: np.ndarray, k_pages: np.ndarray, v_pages: np.ndarray, page_table,
-                     valid_len, scale: float) -> np.ndarray:
+                     valid_len, scale: float, causal: bool = False) -> np.ndarray:
     """O [B, Hq, D] over a paged cache: pools [num_pages, page_size, Hkv, D]
     and page_table [B, pages_per_seq], token t of batch b being row
     t % page_size of page page_table[b, t // page_size] (the paged KV that the
     decode PR page leaves as follow-up work to its identity page table).
 
     The first L = clamp(valid_len[b], 0, pages_per_seq * page_size) tokens are
-    gathered into a contiguous cache and decode_ref's definition applied;
-    rows past L, and pages no valid token maps to, are never read."""
+    gathered into a contiguous cache and decode_ref's definition applied
+    (decode_multi_ref's for q [B, Sq, Hq, D]); rows past L, and pages no
+    valid token maps to, are never read."""
     B = q.shape[0]
     P = k_pages.shape[1]
     page_table = np.asarray(page_table)
     cap = P * page_table.shape[1]
     valid_len = np.broadcast_to(np.asarray(valid_len, dtype=np.int64), (B,))
-    out = np.zeros((B, q.shape[1], v_pages.shape[3]), dtype=np.float64)
+    out = np.zeros(q.shape[:-1] + (v_pages.shape[3],), dtype=np.float64)
     for b in range(B):
         L = int(min(max(int(valid_len[b]), 0), cap))
-        if L == 0:
-            continue
         t = np.arange(L)
         pages, rows = page_table[b, t // P], t % P
         kk, vv = k_pages[pages, rows], v_pages[pages, rows]  # [L, Hkv, D]
-        out[b] = decode_ref(q[b:b + 1], kk[None], vv[None], [L], scale)[0]
+        if q.ndim == 3:
+            out[b] = decode_ref(q[b:b + 1], kk[None], vv[None], [L], scale)[0]
+        else:
+            out[b] = decode_multi_ref(q[b:b + 1], kk[None], vv[None], [L], causal, scale)[0]
     return out
 
 

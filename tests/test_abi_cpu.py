@@ -31,7 +31,8 @@ def test_library_loads_and_exports_header_functions():
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_lse", "fa_fwd_varlen", "fa_fwd_plan",
                           "fa_decode_workspace_bytes", "fa_decode", "fa_decode_paged",
-                          "fa_status_string"}
+                          "fa_decode_multi_workspace_bytes", "fa_decode_multi",
+                          "fa_decode_paged_multi", "fa_status_string"}
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES
@@ -165,6 +166,38 @@ def test_decode_paged_rejects_bad_arguments(kw, code):
 
 def test_decode_paged_empty_batch_is_ok():
     assert paged(B=0) == OK
+
+
+def multi(**kw):
+    a = dict(q=FAKE, kc=FAKE + 0x1000000, vc=FAKE + 0x2000000, vl=FAKE + 0x3000000, cap=4096,
+             o=FAKE + 0x4000000, B=2, Sq=4, Hq=8, Hkv=2, D=128, causal=1, scale=0.1, dtype=0,
+             ws=FAKE + 0x5000000, wsb=None, stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = fa.lib().fa_decode_multi_workspace_bytes(
+            a["B"], max(a["Sq"], 1), a["Hq"], a["Hkv"], a["D"], a["cap"]) or 1
+    return fa.lib().fa_decode_multi(a["q"], a["kc"], a["vc"], a["vl"], a["cap"], a["o"], a["B"],
+                                    a["Sq"], a["Hq"], a["Hkv"], a["D"], a["causal"], a["scale"],
+                                    a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Sq=0), SHAPE), (dict(Sq=33), SHAPE), (dict(q=None), NULL), (dict(cap=0), SHAPE),
+    (dict(wsb=256), WS), (dict(o=FAKE + 0x5000000 - 1024), ALIAS),
+    (dict(o=FAKE + 0x3000000), ALIAS), (dict(D=32), UNSUP),
+])
+def test_decode_multi_rejects_bad_arguments(kw, code):
+    assert multi(**kw) == code
+
+
+def test_decode_multi_workspace_grows_with_tokens():
+    lib = fa.lib()
+    one = lib.fa_decode_workspace_bytes(1, 8, 2, 128, 65536)
+    assert lib.fa_decode_multi_workspace_bytes(1, 1, 8, 2, 128, 65536) == one
+    four = lib.fa_decode_multi_workspace_bytes(1, 4, 8, 2, 128, 65536)
+    assert four >= 4 * one - 4096
+    assert lib.fa_decode_multi_workspace_bytes(1, 0, 8, 2, 128, 65536) == 0
+    assert lib.fa_decode_multi_workspace_bytes(1, 33, 8, 2, 128, 65536) == 0
 
 
 def test_decode_workspace_sizes():

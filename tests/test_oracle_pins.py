@@ -482,3 +482,45 @@ def test_paged_decode_identity_and_shuffled_pools_match_contiguous():
     kbig[perm], vbig[perm] = kp, vp
     got = oracle.decode_paged_ref(q, kbig, vbig, perm.reshape(B, pps), L, 0.3)
     np.testing.assert_allclose(got, want, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# multi-token decode
+# ----------------------------------------------------------------------------
+def test_multi_token_decode_is_the_last_rows_of_causal_prefill():
+    # Sq new tokens at the end of L: the last Sq rows of causal self-attention
+    # over the L tokens, whose queries are the new tokens' queries
+    B, Hq, Hkv, D, cap, Sq = 2, 4, 2, 6, 40, 5
+    kc, vc = rnd((B, cap, Hkv, D), 161), rnd((B, cap, Hkv, D), 162)
+    L = [37, 9]
+    qn = rnd((B, Sq, Hq, D), 163)
+    got = oracle.decode_multi_ref(qn, kc, vc, L, True, 0.45)
+    for b in range(B):
+        qfull = rnd((1, Hq, L[b], D), 164 + b)
+        qfull[0, :, L[b] - Sq:] = qn[b].transpose(1, 0, 2)
+        full = oracle.attention_ref(qfull, kc[b:b + 1, :L[b]].transpose(0, 2, 1, 3),
+                                    vc[b:b + 1, :L[b]].transpose(0, 2, 1, 3), True, 0.45)
+        np.testing.assert_allclose(got[b], full[0, :, L[b] - Sq:].transpose(1, 0, 2), atol=1e-12)
+    # without the mask every token sees all L keys: each token is a plain decode
+    got_nc = oracle.decode_multi_ref(qn, kc, vc, L, False, 0.45)
+    for t in range(Sq):
+        np.testing.assert_allclose(got_nc[:, t], oracle.decode_ref(qn[:, t], kc, vc, L, 0.45),
+                                   atol=1e-12)
+
+
+def test_multi_token_decode_brute_force_and_short_sequences():
+    B, Hq, Hkv, D, cap, Sq = 1, 2, 1, 3, 8, 4
+    kc, vc = rnd((B, cap, Hkv, D), 171), rnd((B, cap, Hkv, D), 172)
+    qn = rnd((B, Sq, Hq, D), 173)
+    for L in (6, 2, 0):
+        got = oracle.decode_multi_ref(qn, kc, vc, [L], True, 0.9)
+        for t in range(Sq):
+            keys = list(range(0, L - Sq + t + 1))
+            for h in range(Hq):
+                if not keys:
+                    assert np.all(got[0, t, h] == 0.0)
+                    continue
+                s = [0.9 * float(np.dot(qn[0, t, h], kc[0, j, 0])) for j in keys]
+                w = [math.exp(x - max(s)) for x in s]
+                want = sum(wi * vc[0, j, 0] for wi, j in zip(w, keys)) / sum(w)
+                np.testing.assert_allclose(got[0, t, h], want, atol=1e-12)
