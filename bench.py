@@ -8,7 +8,8 @@ inputs N(0,1), scale 1/sqrt(128)), with Q/K/V already resident in HBM.
 `value` is useful TFLOP/s: 4*D per admissible (query, key) pair, causal
 pairs only.  The Sq=1 split-KV decode (B1/Hq8/Hkv2/D128, L = 65536,
 NaN-poisoned tail) is timed in the same run and reported as GB/s of
-algorithmic bytes in the "decode" object, and the packed varlen forward on a
+algorithmic bytes in the "decode" object (with the same call through a page
+table and a 4-token causal step), and the packed varlen forward on a
 ragged batch (16 sequences of 256..8192 tokens, Hq32/Hkv8/D128, causal) in
 the "varlen" object.
 
@@ -220,10 +221,31 @@ def bench_decode(fa, torch, steps, warmup):
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
     res["paged"] = {"page_size": P, "us_per_call": us, "GB_s": nbytes / (us * 1e-6) / 1e9}
+    # a multi-token step: 4 query tokens at the end of the same caches, causal
+    Sq = 4
+    q4 = dev(wl.normal_bits((B, Sq, Hq, D), 5004, "bf16"), torch.bfloat16)
+    out4 = torch.empty_like(q4)
+    ws4 = fa.DecodeWorkspace(B, Hq, Hkv, D, cap, Sq=Sq)
+    for i in range(warmup):
+        fa.decode(q4, kcs[i % copies], vcs[i % copies], vl, causal=True, scale=scale, out=out4,
+                  workspace=ws4)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        fa.decode(q4, kcs[i % copies], vcs[i % copies], vl, causal=True, scale=scale, out=out4,
+                  workspace=ws4)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    nb4 = 2 * L * Hkv * D * 2 + 2 * Sq * Hq * D * 2 + 4 * B
+    res["multi"] = {"query_tokens": Sq, "causal": True, "us_per_call": us,
+                    "GB_s": nb4 / (us * 1e-6) / 1e9}
     return {"metric": "bf16 Sq=1 split-KV decode GB/s @B1/Hq8/Hkv2/D128/L65536, NaN tail",
             "value": res["cold"]["GB_s"], "unit": "GB/s", "frac_of_hbm_peak":
             res["cold"]["GB_s"] / HBM_PEAK_GBS, "us_per_call": res["cold"]["us_per_call"],
-            "warm": res["warm"], "paged_cold": res["paged"], "algorithmic_bytes": nbytes,
+            "warm": res["warm"], "paged_cold": res["paged"], "multi_token_cold": res["multi"],
+            "algorithmic_bytes": nbytes,
             "traffic": stored_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)}, \
         (qb, kb, vb, L, scale, first)
 
