@@ -101,7 +101,7 @@ __device__ __forceinline__ void st2_coherent(__amdgpu_buffer_rsrc_t rs, int off,
 // token g / gh, head g % gh of the group; its O row starts at
 // out + out_base + (g / gh) * ostride + (g % gh) * D.  Every thread issues all of its
 // record loads before using any, so a merge costs about one memory round trip.
-template <int D, int DT>
+template <int D, int DT, bool MULTI>
 __device__ void merge_global(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rml, int first,
                              int n, int gg, int cs, int dst, uint16_t* out, long long out_base,
                              int gh, long long ostride, float* lds_scratch) {
@@ -151,8 +151,9 @@ __device__ void merge_global(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t r
       const float dd = den[g];
       const float inv = dd > 0.f ? 1.0f / dd : 0.f;
       const u32x2 pk = {E::pack2(acc[0] * inv, acc[1] * inv), E::pack2(acc[2] * inv, acc[3] * inv)};
-      *reinterpret_cast<u32x2*>(out + out_base + (long long)(g / gh) * ostride +
-                                (long long)(g % gh) * D + 4 * q) = pk;
+      const long long orow =
+          MULTI ? (long long)(g / gh) * ostride + (long long)(g % gh) * D : (long long)g * D;
+      *reinterpret_cast<u32x2*>(out + out_base + orow + 4 * q) = pk;
     } else {
       st4_coherent(ro, ((dst * cs + g) * D + 4 * q) * 4, acc);
     }
@@ -169,7 +170,7 @@ __device__ void merge_global(__amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t r
 // global memory (records of cs columns, written coherently, 16 bytes at a
 // time), or, when `out` is not null, normalise and write O as merge_global
 // does.
-template <int D, int DT>
+template <int D, int DT, bool MULTI>
 __device__ void merge_waves(const float* src_o, const float* src_ml, int n, int gg, int cs,
                             __amdgpu_buffer_rsrc_t ro, __amdgpu_buffer_rsrc_t rml, int dst,
                             uint16_t* out, long long out_base, int gh, long long ostride,
@@ -205,8 +206,9 @@ __device__ void merge_waves(const float* src_o, const float* src_ml, int n, int 
       const float dd = den[g];
       const float inv = dd > 0.f ? 1.0f / dd : 0.f;
       const u32x2 pk = {E::pack2(acc[0] * inv, acc[1] * inv), E::pack2(acc[2] * inv, acc[3] * inv)};
-      *reinterpret_cast<u32x2*>(out + out_base + (long long)(g / gh) * ostride +
-                                (long long)(g % gh) * D + 4 * q) = pk;
+      const long long orow =
+          MULTI ? (long long)(g / gh) * ostride + (long long)(g % gh) * D : (long long)g * D;
+      *reinterpret_cast<u32x2*>(out + out_base + orow + 4 * q) = pk;
     } else {
       st4_coherent(ro, ((dst * cs + g) * D + 4 * q) * 4, acc);
     }
@@ -235,7 +237,7 @@ __device__ __forceinline__ bool take_ticket(unsigned* counter, unsigned total, i
   return *lds_flag != 0;
 }
 
-template <int D, int DT, bool PAGED>
+template <int D, int DT, bool PAGED, bool MULTI>
 __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 8))) void decode_kernel(DecodeParams p) {
   using E = Elt<DT>;
   constexpr int NW = kDecodeWaves;
@@ -254,15 +256,18 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   const int unit = blockIdx.y;
   // a unit's MFMA columns are (query token t, head g of the group): column
   // t * gh + g for t < sq, g < gh, at most 32 of them
-  const int HG = (p.gqa + p.hpg - 1) / p.hpg;
+  // (one query token: MULTI off, sq = 1 and 32 heads per group at compile time)
+  const int sq = MULTI ? p.sq : 1;
+  const int hpg = MULTI ? p.hpg : 32;
+  const int HG = (p.gqa + hpg - 1) / hpg;
   const int hg = unit % HG;
   const int bk = unit / HG;
   const int b = bk / p.Hkv;
   const int hk = bk - b * p.Hkv;
-  const int gh = heads_in_group(p.hpg, p.gqa, hg);
-  const int gg = gh * p.sq;                        // columns in use
-  const int cstride = min(p.hpg, p.gqa) * p.sq;   // columns per record
-  const int hq0 = hk * p.gqa + p.hpg * hg;  // first query head of this group
+  const int gh = heads_in_group(hpg, p.gqa, hg);
+  const int gg = gh * sq;                        // columns in use
+  const int cstride = min(hpg, p.gqa) * sq;     // columns per record
+  const int hq0 = hk * p.gqa + hpg * hg;  // first query head of this group
 
   int L = p.valid_len[b];
   L = min(max(L, 0), p.capacity);
@@ -300,8 +305,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   for (int kk = 0; kk < KSTEPS; ++kk) {
     u32x4 x = {0u, 0u, 0u, 0u};
     if (li < gg) {
-      const int t = li / gh;
-      x = gload16(qg + (((long long)b * p.sq + t) * p.Hq + hq0 + li - t * gh) * D + 16 * kk + 8 * lh);
+      const int t = MULTI ? li / gh : 0;
+      x = gload16(qg + (((long long)b * sq + t) * p.Hq + hq0 + li - t * gh) * D + 16 * kk + 8 * lh);
     }
     if (p.q_sign < 0) x ^= 0x80008000u;
     if (p.q_sign == 0) x = u32x4{0u, 0u, 0u, 0u};
@@ -339,8 +344,8 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   // mask (bottom-right) it sees keys j <= L - sq + t, else every j < L.
   // key_lim is the last key this lane's column sees, mask_from the first key
   // that some column does not see.
-  const int key_lim = p.causal ? L - p.sq + (li < gg ? li / gh : 0) : L - 1;
-  const int mask_from = p.causal ? L - p.sq + 1 : L;
+  const int key_lim = MULTI && p.causal ? L - sq + (li < gg ? li / gh : 0) : L - 1;
+  const int mask_from = MULTI && p.causal ? L - sq + 1 : L;
 
   f32x16 oacc[DTILES];
 #pragma unroll
@@ -497,14 +502,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
       p.part_ml + unit_parts * cstride * 2, (short)0, nrec * cstride * 2 * 4, kBufferFlags);
   uint16_t* og = static_cast<uint16_t*>(p.o);
   // O is [B, sq, Hq, D]: column (t, g) -> row (b, t, hq0 + g)
-  const long long out_base = ((long long)b * p.sq * p.Hq + hq0) * D;
+  const long long out_base = ((long long)b * sq * p.Hq + hq0) * D;
   const long long ostride = (long long)p.Hq * D;
 
   if (p.nsplit == 1) {
-    merge_waves<D, DT>(wo, wml, NW, gg, cstride, ro, rml, 0, og, out_base, gh, ostride, scratch);
+    merge_waves<D, DT, MULTI>(wo, wml, NW, gg, cstride, ro, rml, 0, og, out_base, gh, ostride,
+                              scratch);
     return;
   }
-  merge_waves<D, DT>(wo, wml, NW, gg, cstride, ro, rml, split, nullptr, 0, gh, ostride, scratch);
+  merge_waves<D, DT, MULTI>(wo, wml, NW, gg, cstride, ro, rml, split, nullptr, 0, gh, ostride,
+                            scratch);
   if (kMergeKernel) return;  // the split records are merged by decode_merge_kernel
 
   // ---- level 1: last workgroup of the group merges the group -------------------
@@ -518,14 +525,16 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   int* ticket_flag = reinterpret_cast<int*>(dyn_lds + p.lds_bytes) - 1;
   if (!take_ticket(cnt0 + grp, (unsigned)gsize, ticket_flag)) return;
   if (ngroups == 1) {
-    merge_global<D, DT>(ro, rml, gfirst, gsize, gg, cstride, 0, og, out_base, gh, ostride, scratch);
+    merge_global<D, DT, MULTI>(ro, rml, gfirst, gsize, gg, cstride, 0, og, out_base, gh, ostride,
+                               scratch);
     return;
   }
-  merge_global<D, DT>(ro, rml, gfirst, gsize, gg, cstride, p.nsplit + grp, nullptr, 0, gh, ostride,
-                      scratch);
+  merge_global<D, DT, MULTI>(ro, rml, gfirst, gsize, gg, cstride, p.nsplit + grp, nullptr, 0, gh,
+                             ostride, scratch);
   // ---- level 2: last group merger merges the groups and writes O -----------
   if (!take_ticket(cnt0 + ngroups, (unsigned)ngroups, ticket_flag)) return;
-  merge_global<D, DT>(ro, rml, p.nsplit, ngroups, gg, cstride, 0, og, out_base, gh, ostride, scratch);
+  merge_global<D, DT, MULTI>(ro, rml, p.nsplit, ngroups, gg, cstride, 0, og, out_base, gh, ostride,
+                             scratch);
 }
 
 // Second kernel: merges the nsplit (<= 256, see decode_num_splits) split
@@ -617,7 +626,7 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
   }
 }
 
-template <int D, int DT, bool PAGED>
+template <int D, int DT, bool PAGED, bool MULTI>
 hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   const int HG = (p.gqa + p.hpg - 1) / p.hpg;
   const int gg = min(p.hpg, p.gqa) * p.sq;  // columns per record
@@ -631,7 +640,8 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
   DecodeParams q = p;
   q.lds_bytes = (int)lds;
   dim3 grid(p.nsplit, p.B * p.Hkv * HG);
-  hipLaunchKernelGGL((decode_kernel<D, DT, PAGED>), grid, dim3(kDecodeWaves * 64), lds, stream, q);
+  hipLaunchKernelGGL((decode_kernel<D, DT, PAGED, MULTI>), grid, dim3(kDecodeWaves * 64), lds,
+                     stream, q);
   if (kMergeKernel && p.nsplit > 1) {
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -643,7 +653,11 @@ hipError_t launch_d(const DecodeParams& p, hipStream_t stream) {
 
 template <int D, int DT>
 hipError_t launch_p(const DecodeParams& p, hipStream_t stream) {
-  return p.page_table ? launch_d<D, DT, true>(p, stream) : launch_d<D, DT, false>(p, stream);
+  if (p.sq > 1)
+    return p.page_table ? launch_d<D, DT, true, true>(p, stream)
+                        : launch_d<D, DT, false, true>(p, stream);
+  return p.page_table ? launch_d<D, DT, true, false>(p, stream)
+                      : launch_d<D, DT, false, false>(p, stream);
 }
 
 }  // namespace
