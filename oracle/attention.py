@@ -296,3 +296,42 @@ def varlen_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, cu_q, cu_k, causal: 
         if with_lse:
             lse[:, q0:q1] = lse_ref(qs, ks, causal, scale)[0]
     return (out, lse) if with_lse else out
+
+
+# ----------------------------------------------------------------------------
+# backward pass (gradients of O with respect to Q, K and V)
+# ----------------------------------------------------------------------------
+def attention_bwd_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray, causal: bool,
+                      scale: float):
+    """(dQ, dK, dV) float64 for O = softmax(scale Q K^T + mask) V and an output
+    gradient dO (tessera PR page, flash_attn backward commit: the textbook
+    FA-2 backward -- a pre-pass for D = rowsum(O * dO), dK/dV per key tile,
+    dQ per query tile -- whose plain matrix form is written out here).
+
+    Per (b, h) with kv head hk = h // (Hq/Hkv), in the plain matrix form:
+        P  = softmax(scale Q K^T + mask)          (rows without keys: 0)
+        dV[hk] += P^T dO
+        dP = dO V^T
+        Dr = rowsum(dO * O)  (= rowsum(P * dP))
+        dS = P * (dP - Dr)
+        dQ = scale dS K,     dK[hk] += scale dS^T Q
+    Query heads of one GQA group add into their kv head's dK and dV."""
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    gqa = Hq // Hkv
+    dq = np.zeros_like(q, dtype=np.float64)
+    dk = np.zeros(k.shape, dtype=np.float64)
+    dv = np.zeros(v.shape, dtype=np.float64)
+    allowed = admissible_mask(Sq, Sk, causal)
+    for b in range(B):
+        for h in range(Hq):
+            hk = h // gqa
+            p = probs_ref(q[b, h], k[b, hk], allowed, scale)  # [Sq, Sk]
+            o = p @ v[b, hk]
+            dv[b, hk] += p.T @ do[b, h]
+            dp = do[b, h] @ v[b, hk].T
+            dr = np.sum(do[b, h] * o, axis=1, keepdims=True)
+            ds = p * (dp - dr)
+            dq[b, h] = scale * (ds @ k[b, hk])
+            dk[b, hk] += scale * (ds.T @ q[b, h])
+    return dq, dk, dv

@@ -524,3 +524,103 @@ def test_multi_token_decode_brute_force_and_short_sequences():
                 w = [math.exp(x - max(s)) for x in s]
                 want = sum(wi * vc[0, j, 0] for wi, j in zip(w, keys)) / sum(w)
                 np.testing.assert_allclose(got[0, t, h], want, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# backward pass
+# ----------------------------------------------------------------------------
+BWD_CASES = [
+    # B, Hq, Hkv, Sq, Sk, D, causal
+    (1, 2, 1, 5, 5, 4, True),
+    (2, 2, 2, 4, 7, 3, True),     # bottom-right, Sq < Sk
+    (1, 4, 2, 6, 3, 4, True),     # Sq > Sk: rows without keys
+    (1, 2, 1, 5, 6, 4, False),
+]
+
+
+def _loss_and_grads(case, seed):
+    B, Hq, Hkv, Sq, Sk, D, causal = case
+    q, k, v = rnd((B, Hq, Sq, D), seed), rnd((B, Hkv, Sk, D), seed + 1), rnd((B, Hkv, Sk, D), seed + 2)
+    g = rnd((B, Hq, Sq, D), seed + 3)  # dO: the loss is sum(O * g)
+    return q, k, v, g, causal
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[str(c) for c in BWD_CASES])
+def test_backward_against_finite_differences(case):
+    q, k, v, g, causal = _loss_and_grads(case, 181)
+    scale = 0.6
+    dq, dk, dv = oracle.attention_bwd_ref(q, k, v, g, causal, scale)
+    loss = lambda q_, k_, v_: float(np.sum(oracle.attention_ref(q_, k_, v_, causal, scale) * g))
+    eps = 1e-6
+    rng = np.random.default_rng(182)
+    for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, n)) for n in x.shape)
+            xp, xm = x.copy(), x.copy()
+            xp[idx] += eps
+            xm[idx] -= eps
+            args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+            args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+            fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+            assert abs(fd - grad[idx]) < 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+
+
+@pytest.mark.parametrize("case", BWD_CASES, ids=[str(c) for c in BWD_CASES])
+def test_backward_against_torch_autograd_float64(case):
+    q, k, v, g, causal = _loss_and_grads(case, 191)
+    B, Hq, Hkv, Sq, Sk, D, _ = case
+    scale = 0.45
+    dq, dk, dv = oracle.attention_bwd_ref(q, k, v, g, causal, scale)
+    tq, tk, tv = (torch.tensor(x, requires_grad=True) for x in (q, k, v))
+    kk = tk.repeat_interleave(Hq // Hkv, dim=1)
+    vv = tv.repeat_interleave(Hq // Hkv, dim=1)
+    s = scale * tq @ kk.transpose(-1, -2)
+    mask = torch.arange(Sk)[None, :] <= torch.arange(Sq)[:, None] + (Sk - Sq)
+    if causal:
+        s = s.masked_fill(~mask, -math.inf)
+    p = torch.softmax(s, dim=-1).nan_to_num(0.0)  # rows without keys: 0
+    (p @ vv * torch.tensor(g)).sum().backward()
+    np.testing.assert_allclose(dq, tq.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dk, tk.grad.numpy(), atol=1e-12)
+    np.testing.assert_allclose(dv, tv.grad.numpy(), atol=1e-12)
+
+
+BWD_MUTATIONS = [
+    ("ds = p * (dp - dr)", "ds = p * dp"),                               # dropped D term
+    ("dv[b, hk] += p.T @ do[b, h]", "dv[b, hk] += p @ do[b, h]"),        # transposed P
+    ("dq[b, h] = scale * (ds @ k[b, hk])", "dq[b, h] = (ds @ k[b, hk])"),  # dropped scale
+    ("dk[b, hk] += scale * (ds.T @ q[b, h])", "dk[b, hk] = scale * (ds.T @ q[b, h])"),  # GQA sum lost
+]
+
+
+def _bwd_pins_pass(ns):
+    """Finite differences of sum(O * g) on two tiny cases, rerun on a mutant."""
+    try:
+        for case in (BWD_CASES[0], (1, 4, 2, 5, 5, 3, True)):
+            q, k, v, g, causal = _loss_and_grads(case, 201)
+            dq, dk, dv = ns["attention_bwd_ref"](q, k, v, g, causal, 0.6)
+            loss = lambda q_, k_, v_: float(np.sum(ns["attention_ref"](q_, k_, v_, causal, 0.6) * g))
+            for name, x, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+                it = np.nditer(x, flags=["multi_index"])
+                for _ in it:
+                    idx = it.multi_index
+                    xp, xm = x.copy(), x.copy()
+                    xp[idx] += 1e-6
+                    xm[idx] -= 1e-6
+                    args_p = {"q": (xp, k, v), "k": (q, xp, v), "v": (q, k, xp)}[name]
+                    args_m = {"q": (xm, k, v), "k": (q, xm, v), "v": (q, k, xm)}[name]
+                    fd = (loss(*args_p) - loss(*args_m)) / 2e-6
+                    if abs(fd - grad[idx]) > 1e-6 * max(1.0, abs(fd)):
+                        return False
+        return True
+    except Exception:
+        return False
+
+
+def test_unmutated_backward_oracle_passes_its_pin():
+    assert _bwd_pins_pass(_mutant("", ""))
+
+
+@pytest.mark.parametrize("mutation", BWD_MUTATIONS, ids=[m[1][:30] for m in BWD_MUTATIONS])
+def test_planted_backward_mistake_is_caught(mutation):
+    assert not _bwd_pins_pass(_mutant(*mutation))
