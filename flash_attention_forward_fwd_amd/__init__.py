@@ -15,7 +15,7 @@ import math
 
 from ._lib import (FA_BF16, FA_FP16, FaError, FwdPlan, check, lib)  # noqa: F401
 
-__all__ = ["fwd", "fwd_varlen", "decode", "decode_paged", "fwd_plan", "decode_workspace_bytes", "DecodeWorkspace", "FaError",
+__all__ = ["fwd", "fwd_varlen", "bwd", "decode", "decode_paged", "fwd_plan", "decode_workspace_bytes", "DecodeWorkspace", "FaError",
            "lib", "build"]
 
 
@@ -257,3 +257,41 @@ def decode_paged(q, k_pages, v_pages, page_table, valid_len, causal: bool = Fals
     else:
         check(lib().fa_decode_paged_multi(*args, Sq, *tail), "fa_decode_paged_multi")
     return out
+
+
+def bwd(q, k, v, o, dout, lse, causal: bool = False, scale: float | None = None,
+        dq=None, dk=None, dv=None):
+    """Backward pass: gradients (dq, dk, dv) of o = fwd(q, k, v) for an output
+    gradient dout, from the forward's output o and row log-sum-exp lse
+    (fwd(..., return_lse=True)).  Layouts as fwd; dk/dv add over the query
+    heads of a GQA group."""
+    torch = _torch()
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q, k, v, o, dout must be 4-D [B, H, S, D]")
+    B, Hq, Sq, D = q.shape
+    Hkv, Sk = k.shape[1], k.shape[2]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("bwd needs GPU tensors")
+    for name, t, shape in (("q", q, (B, Hq, Sq, D)), ("k", k, (B, Hkv, Sk, D)),
+                           ("v", v, (B, Hkv, Sk, D)), ("o", o, (B, Hq, Sq, D)),
+                           ("dout", dout, (B, Hq, Sq, D))):
+        _check_tensor(name, t, shape, q.dtype, dev)
+    _check_tensor("lse", lse, (B, Hq, Sq), torch.float32, dev)
+    dq = torch.empty_like(q) if dq is None else dq
+    dk = torch.empty_like(k) if dk is None else dk
+    dv = torch.empty_like(v) if dv is None else dv
+    _check_tensor("dq", dq, (B, Hq, Sq, D), q.dtype, dev)
+    _check_tensor("dk", dk, (B, Hkv, Sk, D), q.dtype, dev)
+    _check_tensor("dv", dv, (B, Hkv, Sk, D), q.dtype, dev)
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    n = int(lib().fa_bwd_workspace_bytes(B, Hq, Sq))
+    buf = torch.empty(n + 256, dtype=torch.uint8, device=dev)
+    ws = buf.data_ptr() + (-buf.data_ptr()) % 256
+    st = lib().fa_bwd(q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(), dout.data_ptr(),
+                      lse.data_ptr(), dq.data_ptr(), dk.data_ptr(), dv.data_ptr(), B, Hq, Hkv,
+                      Sq, Sk, D, int(bool(causal)), float(scale), _dtype_code(q), ws, n,
+                      _stream_ptr(q))
+    check(st, "fa_bwd")
+    return dq, dk, dv

@@ -40,6 +40,9 @@ SIGNATURES = {
                              ctypes.c_size_t, _P]),
     "fa_decode_paged_multi": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _I, _I, _I, _I, _I, _F,
                                    _I, _P, ctypes.c_size_t, _P]),
+    "fa_bwd_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I]),
+    "fa_bwd": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P,
+                    ctypes.c_size_t, _P]),
     "fa_status_string": (ctypes.c_char_p, [_I]),
 }
 

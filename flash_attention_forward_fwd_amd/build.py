@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 ARCH = "gfx950"
 
-SOURCES = ["fa_api.cpp", "fa_prefill.hip", "fa_decode.hip"]
+SOURCES = ["fa_api.cpp", "fa_prefill.hip", "fa_decode.hip", "fa_backward.hip"]
 
 # Packed fp32 VALU forms are kept out of the generated code on purpose.
 DEVICE_FLAGS = ["-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]

@@ -330,6 +330,70 @@ fa_status_t paged_impl(const void* q, const void* k_pages, const void* v_pages,
                      workspace, workspace_bytes, stream);
 }
 
+size_t bwd_workspace_bytes(long long rows) { return (size_t)((rows * 4 + 255) / 256 * 256); }
+
+fa_status_t bwd_impl(const void* q, const void* k, const void* v, const void* o,
+                     const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                     int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale, int dtype,
+                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return FA_ERR_SCALE;
+  long long nq, nkv, rows;
+  if (!count4(B, Hq, Sq, D, &nq) || !count4(B, Hkv, Sk, D, &nkv) || !count4(B, Hq, Sq, 1, &rows))
+    return FA_ERR_SHAPE;
+  if (nq > LLONG_MAX / 4 || nkv > LLONG_MAX / 4) return FA_ERR_SHAPE;
+  // workgroup counts of the three launches fit a grid dimension
+  if (rows / 32 + 1 > INT_MAX || (long long)B * Hq * ((Sq + 127) / 128) > INT_MAX ||
+      (long long)B * Hkv * ((Sk + 127) / 128) > INT_MAX)
+    return FA_ERR_SHAPE;
+  if (nq > 0 && (!q || !o || !dout || !lse || !dq)) return FA_ERR_NULL;
+  if (nkv > 0 && (!k || !v || !dk || !dv)) return FA_ERR_NULL;
+  for (const void* ptr : {q, k, v, o, dout, static_cast<const void*>(dq),
+                          static_cast<const void*>(dk), static_cast<const void*>(dv)})
+    if (ptr && !aligned16(ptr)) return FA_ERR_ALIGN;
+  if (lse && (reinterpret_cast<uintptr_t>(lse) & 3u) != 0) return FA_ERR_ALIGN;
+  const size_t need = bwd_workspace_bytes(rows);
+  if (rows > 0 && (!workspace || workspace_bytes < need ||
+                   (reinterpret_cast<uintptr_t>(workspace) & 255u) != 0))
+    return FA_ERR_WORKSPACE;
+  const long long qb = nq * 2, kb = nkv * 2, lb = rows * 4;
+  const void* ins[] = {q, k, v, o, dout, lse, workspace};
+  const long long insz[] = {qb, kb, kb, qb, qb, lb, (long long)need};
+  const void* outs[] = {dq, dk, dv};
+  const long long outsz[] = {qb, kb, kb};
+  for (int i = 0; i < 3; ++i) {
+    for (int j = 0; j < 7; ++j)
+      if (overlaps(outs[i], outsz[i], ins[j], insz[j])) return FA_ERR_ALIAS;
+    for (int j = i + 1; j < 3; ++j)
+      if (overlaps(outs[i], outsz[i], outs[j], outsz[j])) return FA_ERR_ALIAS;
+  }
+  if (B == 0 || (Sq == 0 && Sk == 0)) return FA_OK;  // nothing to write
+  fa::BwdParams p;
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.dout = dout;
+  p.lse = lse;
+  p.dsum = static_cast<float*>(workspace);
+  p.dq = dq;
+  p.dk = dk;
+  p.dv = dv;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Sk = Sk;
+  p.gqa = Hq / Hkv;
+  fold_scale(scale, &p.c_log2, &p.q_sign);
+  p.scale = scale;
+  const hipError_t e =
+      fa::launch_backward(p, D, dtype, causal != 0, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? FA_OK : FA_ERR_HIP;
+}
+
 }  // namespace
 
 extern "C" {
@@ -411,6 +475,20 @@ fa_status_t fa_decode_paged_multi(const void* q, const void* k_pages, const void
   return paged_impl(q, k_pages, v_pages, page_table, valid_len, page_size, pages_per_seq,
                     num_pages, o, B, Sq, Hq, Hkv, D, causal, scale, dtype, workspace,
                     workspace_bytes, stream);
+}
+
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq) {
+  long long rows;
+  if (B < 0 || Hq < 1 || Sq < 0 || !count4(B, Hq, Sq, 1, &rows)) return 0;
+  return bwd_workspace_bytes(rows);
+}
+
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int Hq, int Hkv, int Sq,
+                   int Sk, int D, int causal, float scale, int dtype, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  return bwd_impl(q, k, v, o, dout, lse, dq, dk, dv, B, Hq, Hkv, Sq, Sk, D, causal, scale, dtype,
+                  workspace, workspace_bytes, stream);
 }
 
 const char* fa_status_string(int status) {

@@ -1,0 +1,372 @@
+// Attention backward pass for gfx950: dQ, dK, dV of O = softmax(scale Q K^T +
+// mask) V given dO and the forward's row log-sum-exp, as three kernels in the
+// textbook FA-2 split (tessera PR page, flash_attn backward commit: a pre-pass
+// for D = rowsum(O * dO), dK/dV per key tile, dQ per query tile; P and dS are
+// recomputed tile by tile, no score matrix is stored):
+//
+//   pre   D_i = sum_d dO[i,d] O[i,d]                                 (fp32)
+//   dq    per 128 query rows: S^T = K Q^T, dP^T = V dO^T,
+//         P = exp2(S c - LSE_i log2 e), dS = P (dP - D_i),
+//         dQ^T += K^T dS^T                       (Q and dO stay in registers)
+//   dkdv  per 128 keys: S = Q K^T, dP = dO V^T, P and dS as above,
+//         dV^T += dO^T P, dK^T += Q^T dS   (K and V stay in registers; the
+//         query heads of a GQA group add into their kv head in the loop, so
+//         no atomics are needed anywhere)
+//
+// Every product runs on the 32x32x16 matrix core with the operand layouts of
+// the forward kernel: a wave owns 32 rows (dq) or 32 keys (dkdv), the operand
+// that varies along the loop is read from LDS, transposed operands come from
+// the gfx950 transposing LDS read, and P / dS feed the next product straight
+// from the accumulator registers in their register order.  Tiles are staged
+// global -> registers -> LDS with one barrier on each side; this version
+// favours simplicity over overlap.
+#include "fa_common.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kBwdWaves = 4;        // waves per workgroup, 32 rows or keys each
+constexpr int kRowPad = 8;          // pad of tiles read by 16-byte row reads only
+constexpr int kTrPad = 32;          // pad of tiles that are also read transposed
+
+// Copy `valid` rows (row stride D elements in global memory) of a ROWS x D tile
+// into LDS rows of LST elements; rows past `valid` are zero.  q_sign (+1, -1,
+// 0) is applied to every element (sign bit flipped, or zeroed).
+template <int D, int ROWS, int LST>
+__device__ __forceinline__ void stage_tile(uint16_t* lds, const uint16_t* src, int valid,
+                                           int q_sign) {
+  constexpr int CH = D / 8;
+  for (int c = threadIdx.x; c < ROWS * CH; c += blockDim.x) {
+    const int r = c / CH, cc = c - r * CH;
+    u32x4 x = {0u, 0u, 0u, 0u};
+    if (r < valid) x = gload16(src + (long long)r * D + cc * 8);
+    if (q_sign < 0) x ^= 0x80008000u;
+    if (q_sign == 0) x = u32x4{0u, 0u, 0u, 0u};
+    lds_write16(lds + r * LST + cc * 8, x);
+  }
+}
+
+// ---- pre: D_i = rowsum(dO * O), 8 threads per row ------------------------------
+template <int D, int DT>
+__global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
+  using E = Elt<DT>;
+  constexpr int PER = D / 8;  // elements per thread
+  const long long rows = (long long)p.B * p.Hq * p.Sq;
+  const long long row = (long long)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int part = threadIdx.x & 7;
+  float acc = 0.f;
+  if (row < rows) {
+    const uint16_t* o = static_cast<const uint16_t*>(p.o) + row * D + part * PER;
+    const uint16_t* g = static_cast<const uint16_t*>(p.dout) + row * D + part * PER;
+#pragma unroll
+    for (int c = 0; c < PER; c += 8) {
+      const u32x4 a = gload16(o + c), b = gload16(g + c);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc += E::widen((unsigned short)(a[i] & 0xFFFFu)) * E::widen((unsigned short)(b[i] & 0xFFFFu));
+        acc += E::widen((unsigned short)(a[i] >> 16)) * E::widen((unsigned short)(b[i] >> 16));
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 1);
+  acc += __shfl_xor(acc, 2);
+  acc += __shfl_xor(acc, 4);
+  if (row < rows && part == 0) p.dsum[row] = acc;
+}
+
+// ---- dq: one workgroup per (batch, query head, 128 query rows) ------------------
+template <int D, int DT, bool CAUSAL>
+__global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
+void bwd_dq_kernel(BwdParams p) {
+  using E = Elt<DT>;
+  constexpr int BN = 64;                 // keys per tile (two 32-key sub-tiles)
+  constexpr int KSTEPS = D / 16, DTILES = D / 32;
+  constexpr int KST = D + kTrPad;        // K: row reads (S) and transposed reads (dQ)
+  constexpr int VST = D + kRowPad;       // V: row reads (dP)
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KST];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * VST];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int li = lane & 31, lh = lane >> 5, ti = lane & 15;
+  const int nqb = (p.Sq + 127) / 128;
+  int blk = blockIdx.x;
+  const int qb = blk % nqb;
+  blk /= nqb;
+  const int hq = blk % p.Hq;
+  const int b = blk / p.Hq;
+  const int hk = hq / p.gqa;
+  const int q0 = qb * 128, rw0 = q0 + wave * 32, row = rw0 + li;
+  const int Sq = p.Sq, Sk = p.Sk, kv_off = Sk - Sq;
+  const long long qbase = ((long long)b * p.Hq + hq) * Sq * D;   // q, dO, dQ
+  const long long kvbase = ((long long)b * p.Hkv + hk) * Sk * D;
+  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + kvbase;
+  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + kvbase;
+
+  // Q (sign-folded) and dO rows as B operands: lane row li, d = 16 kk + 8 lh + e
+  u32x4 qr[KSTEPS], gr[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (row < Sq) {
+      x = gload16(static_cast<const uint16_t*>(p.q) + qbase + (long long)row * D + 16 * kk + 8 * lh);
+      y = gload16(static_cast<const uint16_t*>(p.dout) + qbase + (long long)row * D + 16 * kk +
+                  8 * lh);
+    }
+    if (p.q_sign < 0) x ^= 0x80008000u;
+    if (p.q_sign == 0) x = u32x4{0u, 0u, 0u, 0u};
+    qr[kk] = x;
+    gr[kk] = y;
+  }
+  const long long srow = ((long long)b * p.Hq + hq) * Sq + row;
+  const float lse2 = row < Sq ? p.lse[srow] * kLog2e : 0.f;
+  const float dr = row < Sq ? p.dsum[srow] : 0.f;
+  const float c = p.c_log2;
+
+  int kv_end = Sk, wave_end = Sk;
+  if (CAUSAL) {
+    kv_end = min(max(min(Sq, q0 + 128) + kv_off, 0), Sk);
+    wave_end = min(max(min(Sq, rw0 + 32) + kv_off, 0), Sk);
+  }
+  if (rw0 >= Sq) wave_end = 0;
+  const int ntiles = (kv_end + BN - 1) / BN;
+  const int v_lane = (4 * lh + (ti >> 2)) * KST + 16 * ((lane >> 4) & 1) + 4 * (ti & 3);
+
+  f32x16 dq[DTILES];
+#pragma unroll
+  for (int dt = 0; dt < DTILES; ++dt) dq[dt] = f32x16{};
+
+  for (int t = 0; t < ntiles; ++t) {
+    __syncthreads();  // the previous tile is no longer read
+    const int valid = min(BN, Sk - t * BN);
+    stage_tile<D, BN, KST>(Ks, kg + (long long)t * BN * D, valid, 1);
+    stage_tile<D, BN, VST>(Vs, vg + (long long)t * BN * D, valid, 1);
+    __syncthreads();
+    if (t * BN >= wave_end) continue;
+    f32x16 S[2], dP[2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      S[st] = f32x16{};
+      dP[st] = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        S[st] = E::mfma(lds_read16(Ks + (32 * st + li) * KST + 16 * kk + 8 * lh), qr[kk], S[st]);
+        dP[st] = E::mfma(lds_read16(Vs + (32 * st + li) * VST + 16 * kk + 8 * lh), gr[kk], dP[st]);
+      }
+    }
+    // lane = query row; register r of sub-tile st is key t*BN + 32 st + 8 (r/4) + 4 lh + r%4
+    u32x4 db[2][2];
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int key = t * BN + 32 * st + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const bool ok = row < Sq && key < Sk && (!CAUSAL || key <= row + kv_off);
+        const float pr = ok ? fast_exp2(__builtin_fmaf(S[st][r], c, -lse2)) : 0.f;
+        S[st][r] = pr * (dP[st][r] - dr);
+      }
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int r0 = 8 * kk;
+        db[st][kk] = u32x4{E::pack2(S[st][r0 + 0], S[st][r0 + 1]), E::pack2(S[st][r0 + 2], S[st][r0 + 3]),
+                           E::pack2(S[st][r0 + 4], S[st][r0 + 5]), E::pack2(S[st][r0 + 6], S[st][r0 + 7])};
+      }
+    }
+    // dQ^T += K^T dS^T: K^T by transposing reads, keys in dS's register order
+#pragma unroll
+    for (int st = 0; st < 2; ++st)
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt) {
+          const uint16_t* kr = Ks + v_lane + (32 * st + 16 * kk) * KST + 32 * dt;
+          const u32x2 lo = lds_read_tr16(kr);
+          const u32x2 hi = lds_read_tr16(kr + 8 * KST);
+          dq[dt] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, db[st][kk], dq[dt]);
+        }
+  }
+
+  // dQ = scale * (dS K): lane row li, d = 32 dt + 8 (r/4) + 4 lh + r%4
+  if (row < Sq) {
+    uint16_t* orow = static_cast<uint16_t*>(p.dq) + qbase + (long long)row * D + 4 * lh;
+    const float sc = p.scale;
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const u32x2 pk = {E::pack2(dq[dt][4 * a + 0] * sc, dq[dt][4 * a + 1] * sc),
+                          E::pack2(dq[dt][4 * a + 2] * sc, dq[dt][4 * a + 3] * sc)};
+        *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * a) = pk;
+      }
+  }
+}
+
+// ---- dkdv: one workgroup per (batch, kv head, 128 keys) -------------------------
+template <int D, int DT, bool CAUSAL>
+__global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void bwd_dkdv_kernel(BwdParams p) {
+  using E = Elt<DT>;
+  constexpr int BM = 32;                 // query rows per step
+  constexpr int KSTEPS = D / 16, DTILES = D / 32;
+  constexpr int QST = D + kTrPad;        // Q and dO: row reads and transposed reads
+  __shared__ __attribute__((aligned(16))) uint16_t Qs[BM * QST];
+  __shared__ __attribute__((aligned(16))) uint16_t Gs[BM * QST];
+  __shared__ float Ls[BM], Ds[BM];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = uniform(tid >> 6);
+  const int li = lane & 31, lh = lane >> 5, ti = lane & 15;
+  const int nkb = (p.Sk + 127) / 128;
+  int blk = blockIdx.x;
+  const int kb = blk % nkb;
+  blk /= nkb;
+  const int hk = blk % p.Hkv;
+  const int b = blk / p.Hkv;
+  const int k0 = kb * 128, kw0 = k0 + wave * 32, key = kw0 + li;
+  const int Sq = p.Sq, Sk = p.Sk, kv_off = Sk - Sq;
+  const long long kvbase = ((long long)b * p.Hkv + hk) * Sk * D;
+
+  // K and V rows as B operands: lane key li, d = 16 kk + 8 lh + e
+  u32x4 kr[KSTEPS], vr[KSTEPS];
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
+    if (key < Sk) {
+      x = gload16(static_cast<const uint16_t*>(p.k) + kvbase + (long long)key * D + 16 * kk + 8 * lh);
+      y = gload16(static_cast<const uint16_t*>(p.v) + kvbase + (long long)key * D + 16 * kk + 8 * lh);
+    }
+    kr[kk] = x;
+    vr[kk] = y;
+  }
+  const float c = p.c_log2;
+  const int v_lane = (4 * lh + (ti >> 2)) * QST + 16 * ((lane >> 4) & 1) + 4 * (ti & 3);
+
+  f32x16 dk[DTILES], dv[DTILES];
+#pragma unroll
+  for (int dt = 0; dt < DTILES; ++dt) {
+    dk[dt] = f32x16{};
+    dv[dt] = f32x16{};
+  }
+
+  // rows that see a key of this block: row + kv_off >= k0 when causal
+  const int r_first = CAUSAL ? (max(0, k0 - kv_off) / BM) * BM : 0;
+  for (int g = 0; g < p.gqa; ++g) {
+    const int hq = hk * p.gqa + g;
+    const long long qbase = ((long long)b * p.Hq + hq) * Sq * D;
+    const long long sbase = ((long long)b * p.Hq + hq) * Sq;
+    for (int r0 = r_first; r0 < Sq; r0 += BM) {
+      __syncthreads();  // the previous tile is no longer read
+      const int valid = min(BM, Sq - r0);
+      stage_tile<D, BM, QST>(Qs, static_cast<const uint16_t*>(p.q) + qbase + (long long)r0 * D,
+                             valid, p.q_sign);
+      stage_tile<D, BM, QST>(Gs, static_cast<const uint16_t*>(p.dout) + qbase + (long long)r0 * D,
+                             valid, 1);
+      if (tid < BM) {
+        const int r = r0 + tid;
+        Ls[tid] = r < Sq ? p.lse[sbase + r] * kLog2e : 0.f;
+        Ds[tid] = r < Sq ? p.dsum[sbase + r] : 0.f;
+      }
+      __syncthreads();
+      if (kw0 >= Sk) continue;                            // no keys in this wave
+      if (CAUSAL && kw0 > r0 + BM - 1 + kv_off) continue;  // every pair masked
+      f32x16 S = f32x16{}, dP = f32x16{};
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk) {
+        S = E::mfma(lds_read16(Qs + li * QST + 16 * kk + 8 * lh), kr[kk], S);
+        dP = E::mfma(lds_read16(Gs + li * QST + 16 * kk + 8 * lh), vr[kk], dP);
+      }
+      // lane = key; register r is query row r0 + 8 (r/4) + 4 lh + r%4
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int rr = 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int rowi = r0 + rr;
+        const bool ok = rowi < Sq && key < Sk && (!CAUSAL || key <= rowi + kv_off);
+        const float pr = ok ? fast_exp2(__builtin_fmaf(S[r], c, -Ls[rr])) : 0.f;
+        S[r] = pr;
+        dP[r] = pr * (dP[r] - Ds[rr]);
+      }
+      u32x4 pb[2], db[2];
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk) {
+        const int q = 8 * kk;
+        pb[kk] = u32x4{E::pack2(S[q + 0], S[q + 1]), E::pack2(S[q + 2], S[q + 3]),
+                       E::pack2(S[q + 4], S[q + 5]), E::pack2(S[q + 6], S[q + 7])};
+        db[kk] = u32x4{E::pack2(dP[q + 0], dP[q + 1]), E::pack2(dP[q + 2], dP[q + 3]),
+                       E::pack2(dP[q + 4], dP[q + 5]), E::pack2(dP[q + 6], dP[q + 7])};
+      }
+      // dV^T += dO^T P and dK^T += Q^T dS: dO^T, Q^T by transposing reads,
+      // rows in the register order of P and dS
+#pragma unroll
+      for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt) {
+          const int off = v_lane + 16 * kk * QST + 32 * dt;
+          const u32x2 glo = lds_read_tr16(Gs + off), ghi = lds_read_tr16(Gs + off + 8 * QST);
+          dv[dt] = E::mfma(u32x4{glo[0], glo[1], ghi[0], ghi[1]}, pb[kk], dv[dt]);
+          const u32x2 qlo = lds_read_tr16(Qs + off), qhi = lds_read_tr16(Qs + off + 8 * QST);
+          dk[dt] = E::mfma(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, db[kk], dk[dt]);
+        }
+    }
+  }
+
+  // dK = scale * (dS^T Q) (Q was sign-folded: scale * q_sign restores it),
+  // dV = P^T dO: lane key li, d = 32 dt + 8 (r/4) + 4 lh + r%4
+  if (key < Sk) {
+    uint16_t* krow = static_cast<uint16_t*>(p.dk) + kvbase + (long long)key * D + 4 * lh;
+    uint16_t* vrow = static_cast<uint16_t*>(p.dv) + kvbase + (long long)key * D + 4 * lh;
+    const float sc = p.scale * (float)p.q_sign;
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const u32x2 pk = {E::pack2(dk[dt][4 * a + 0] * sc, dk[dt][4 * a + 1] * sc),
+                          E::pack2(dk[dt][4 * a + 2] * sc, dk[dt][4 * a + 3] * sc)};
+        *reinterpret_cast<u32x2*>(krow + 32 * dt + 8 * a) = pk;
+        const u32x2 pv = {E::pack2(dv[dt][4 * a + 0], dv[dt][4 * a + 1]),
+                          E::pack2(dv[dt][4 * a + 2], dv[dt][4 * a + 3])};
+        *reinterpret_cast<u32x2*>(vrow + 32 * dt + 8 * a) = pv;
+      }
+  }
+}
+
+template <int D, int DT, bool CAUSAL>
+hipError_t launch_bwd_c(const BwdParams& p, hipStream_t stream) {
+  // Sq = 0 still writes dK = dV = 0, Sk = 0 still writes dQ = 0
+  const long long rows = (long long)p.B * p.Hq * p.Sq;
+  const int nqb = (p.Sq + 127) / 128, nkb = (p.Sk + 127) / 128;
+  if (rows > 0) {
+    hipLaunchKernelGGL((bwd_pre_kernel<D, DT>), dim3((unsigned)((rows + 31) / 32)), dim3(256), 0,
+                       stream, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((bwd_dq_kernel<D, DT, CAUSAL>), dim3(p.B * p.Hq * nqb),
+                       dim3(kBwdWaves * 64), 0, stream, p);
+    const hipError_t e2 = hipGetLastError();
+    if (e2 != hipSuccess) return e2;
+  }
+  if (nkb > 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, CAUSAL>), dim3(p.B * p.Hkv * nkb),
+                       dim3(kBwdWaves * 64), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <int D, int DT>
+hipError_t launch_bwd_d(const BwdParams& p, bool causal, hipStream_t stream) {
+  return causal ? launch_bwd_c<D, DT, true>(p, stream) : launch_bwd_c<D, DT, false>(p, stream);
+}
+
+}  // namespace
+
+hipError_t launch_backward(const BwdParams& p, int D, int dtype, bool causal,
+                           hipStream_t stream) {
+  if (D == 128) {
+    return dtype == kBF16 ? launch_bwd_d<128, kBF16>(p, causal, stream)
+                          : launch_bwd_d<128, kFP16>(p, causal, stream);
+  }
+  return dtype == kBF16 ? launch_bwd_d<64, kBF16>(p, causal, stream)
+                        : launch_bwd_d<64, kFP16>(p, causal, stream);
+}
+
+}  // namespace fa

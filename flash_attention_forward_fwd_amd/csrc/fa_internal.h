@@ -90,4 +90,27 @@ size_t decode_workspace_layout(int B, int Sq, int Hq, int Hkv, int D, int capaci
                                size_t* off_ml, size_t* off_tickets);
 hipError_t launch_decode(const DecodeParams& p, int D, int dtype, hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// Backward (dQ, dK, dV)
+// ---------------------------------------------------------------------------
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;    // [B, Hq, Sq] natural-log row log-sum-exp of the forward
+  float* dsum;         // [B, Hq, Sq] workspace: rowsum(dO * O)
+  void* dq;
+  void* dk;
+  void* dv;
+  int B, Hq, Hkv, Sq, Sk;
+  int gqa;
+  float c_log2;        // |scale| * log2(e), or 1 when scale == 0
+  int q_sign;          // +1, -1, or 0 (scale == 0), applied to q in the kernels
+  float scale;
+};
+
+hipError_t launch_backward(const BwdParams& p, int D, int dtype, bool causal, hipStream_t stream);
+
 }  // namespace fa

@@ -231,6 +231,31 @@ fa_status_t fa_decode_paged_multi(const void* q, const void* k_pages, const void
                                   float scale, int dtype, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/*
+ * Backward pass: gradients of O = softmax(scale Q K^T + mask) V (tessera PR
+ * page, flash_attn backward commit: the FA-2 backward as a pre-pass for
+ * D = rowsum(O * dO), a dK/dV pass per key tile and a dQ pass per query tile).
+ *   q, k, v   : the forward's inputs, layouts as fa_fwd
+ *   o         : [B, Hq, Sq, D] the forward's output
+ *   dout      : [B, Hq, Sq, D] gradient of the loss with respect to o
+ *   lse       : [B, Hq, Sq] float32, the forward's row log-sum-exp (fa_fwd_lse)
+ *   dq        : [B, Hq, Sq, D]  written
+ *   dk, dv    : [B, Hkv, Sk, D] written; the query heads of a GQA group add
+ *               into their kv head
+ *   workspace : device memory of at least fa_bwd_workspace_bytes(B, Hq, Sq)
+ *               bytes, 256-byte aligned (holds the row sums D; no zeroing needed)
+ * causal, scale, dtype as fa_fwd.  Sq = 0 gives dK = dV = 0; Sk = 0 gives dQ = 0.
+ * Errors: as fa_fwd, FA_ERR_WORKSPACE for a missing or small workspace, and
+ * FA_ERR_ALIAS when an output overlaps an input, the workspace or another
+ * output.  Runs as three kernels on `stream`; allocates nothing.
+ */
+size_t fa_bwd_workspace_bytes(int B, int Hq, int Sq);
+
+fa_status_t fa_bwd(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
+                   int dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Human-readable name of a status code (static storage). */
 const char* fa_status_string(int status);
 

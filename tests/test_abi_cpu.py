@@ -32,7 +32,8 @@ def test_library_loads_and_exports_header_functions():
     assert set(names) == {"fa_fwd", "fa_fwd_lse", "fa_fwd_varlen", "fa_fwd_plan",
                           "fa_decode_workspace_bytes", "fa_decode", "fa_decode_paged",
                           "fa_decode_multi_workspace_bytes", "fa_decode_multi",
-                          "fa_decode_paged_multi", "fa_status_string"}
+                          "fa_decode_paged_multi", "fa_bwd_workspace_bytes", "fa_bwd",
+                          "fa_status_string"}
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES
@@ -198,6 +199,37 @@ def test_decode_multi_workspace_grows_with_tokens():
     assert four >= 4 * one - 4096
     assert lib.fa_decode_multi_workspace_bytes(1, 0, 8, 2, 128, 65536) == 0
     assert lib.fa_decode_multi_workspace_bytes(1, 33, 8, 2, 128, 65536) == 0
+
+
+def bwd(**kw):
+    a = dict(q=FAKE, k=FAKE + 0x1000000, v=FAKE + 0x2000000, o=FAKE + 0x3000000,
+             g=FAKE + 0x4000000, lse=FAKE + 0x5000000, dq=FAKE + 0x6000000, dk=FAKE + 0x7000000,
+             dv=FAKE + 0x8000000, B=1, Hq=4, Hkv=2, Sq=128, Sk=128, D=128, causal=1, scale=0.1,
+             dtype=0, ws=FAKE + 0x9000000, wsb=None, stream=None)
+    a.update(kw)
+    if a["wsb"] is None:
+        a["wsb"] = fa.lib().fa_bwd_workspace_bytes(max(a["B"], 0), max(a["Hq"], 1),
+                                                   max(a["Sq"], 0)) or 1
+    return fa.lib().fa_bwd(a["q"], a["k"], a["v"], a["o"], a["g"], a["lse"], a["dq"], a["dk"],
+                           a["dv"], a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Sk"], a["D"],
+                           a["causal"], a["scale"], a["dtype"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(lse=None), NULL), (dict(dk=None), NULL), (dict(g=None), NULL),
+    (dict(B=-1), SHAPE), (dict(Hq=6, Hkv=4), SHAPE), (dict(D=96), UNSUP), (dict(dtype=7), UNSUP),
+    (dict(scale=float("nan")), SCALE), (dict(dq=FAKE + 0x6000008), ALIGN),
+    (dict(lse=FAKE + 0x5000002), ALIGN), (dict(ws=None), WS), (dict(wsb=8), WS),
+    (dict(ws=FAKE + 0x9000010), WS), (dict(dq=FAKE), ALIAS), (dict(dk=FAKE + 0x6000000), ALIAS),
+    (dict(dv=FAKE + 0x9000000), ALIAS), (dict(dq=FAKE + 0x5000000), ALIAS),
+])
+def test_bwd_rejects_bad_arguments(kw, code):
+    assert bwd(**kw) == code
+
+
+def test_bwd_empty_is_ok():
+    assert bwd(B=0) == OK
+    assert bwd(Sq=0, Sk=0) == OK
 
 
 def test_decode_workspace_sizes():
