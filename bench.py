@@ -101,7 +101,7 @@ def worst_frac(got, ref):
     return float(np.max(np.abs(got - ref) / (1e-2 + 1e-2 * np.abs(ref)))) if got.size else 0.0
 
 
-def cpu_leg(prefill, decode, varlen, heads):
+def cpu_leg(prefill, decode, varlen, heads, backward=None):
     """The CPU oracle, as it stands, on this host.
 
     Times it over `heads` whole query heads of the prefill workload (the CPU
@@ -156,6 +156,25 @@ def cpu_leg(prefill, decode, varlen, heads):
                                           vs.causal, vs.scale, 0, h, rows)
             worst = max(worst, worst_frac(oracle.widen(vout[q0 + rows, h], vs.dtype), r))
         parity["varlen_sampled_worst_frac"] = worst
+    if backward is not None:
+        # sampled dQ rows of the backward against the oracle (bound scaled by
+        # the sample's largest gradient, as in the backward tests)
+        g, dq_bits = backward
+        gf = oracle.widen(g, s.dtype)
+        rng = np.random.default_rng(17)
+        worst = 0.0
+        for h in (0, s.Hq // 2 + 3, s.Hq - 1):
+            rows = np.unique(np.concatenate([[0, s.Sq - 1], rng.integers(0, s.Sq, 6)]))
+            qh = oracle.widen(q[:, h:h + 1], s.dtype)
+            hk = h // gqa
+            kh, vh = oracle.widen(k[:, hk:hk + 1], s.dtype), oracle.widen(v[:, hk:hk + 1], s.dtype)
+            r = oracle.attention_bwd_dq_rows_ref(qh, kh, vh, gf[:, h:h + 1], s.causal, s.scale, 0,
+                                                 0, rows)
+            got = oracle.widen(dq_bits[0, h, rows], s.dtype)
+            bound = 1e-2 * np.max(np.abs(r)) + 1e-2 * np.abs(r) + 1e-12
+            worst = max(worst, float(np.max(np.abs(got - r) / bound)) if np.all(np.isfinite(got))
+                        else float("inf"))
+        parity["backward_dq_sampled_worst_frac"] = worst
     bad = {key: val for key, val in parity.items() if key.endswith("frac") and not val <= 1.0}
     if bad:
         raise SystemExit(f"parity check failed: {bad}")
@@ -292,6 +311,36 @@ def bench_varlen(fa, torch, steps, warmup):
         (q, k, v, first, s)
 
 
+def bench_backward(fa, torch, q, k, v, tq, tk, tv, s, steps, warmup):
+    """The backward pass at the headline shape for a seeded N(0,1) output
+    gradient: useful TFLOP/s at 10*D per admissible pair (the five products
+    S, dP, dV, dK, dQ of 2*D each)."""
+    import workloads as wl
+    g = wl.normal_bits((s.B, s.Hq, s.Sq, s.D), s.seed_base + 3, s.dtype)
+    tg = dev(g, torch.bfloat16)
+    o, lse = fa.fwd(tq, tk, tv, causal=s.causal, scale=s.scale, return_lse=True)
+    dq, dk, dv = fa.bwd(tq, tk, tv, o, tg, lse, causal=s.causal, scale=s.scale)
+    torch.cuda.synchronize()
+    first = host_bits(dq)
+    for _ in range(warmup):
+        fa.bwd(tq, tk, tv, o, tg, lse, causal=s.causal, scale=s.scale, dq=dq, dk=dk, dv=dv)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fa.bwd(tq, tk, tv, o, tg, lse, causal=s.causal, scale=s.scale, dq=dq, dk=dk, dv=dv)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    flop = 10 * s.D * s.B * s.Hq * s.admissible_pairs_per_head()
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"metric": "bf16 causal FA backward TFLOP/s @Hq128/Hkv8/D128/Sq8192 (10*D per pair)",
+            "value": round(tf, 2), "unit": "TFLOP/s",
+            "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4), "ms_per_call": round(ms, 3),
+            "useful_flop": flop}, (g, first)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +351,8 @@ def main():
     ap.add_argument("--decode", type=int, default=1, help="also time decode (1) or not (0)")
     ap.add_argument("--varlen", type=int, default=1,
                     help="also time the packed varlen forward (1) or not (0)")
+    ap.add_argument("--backward", type=int, default=1,
+                    help="also time the backward pass (1) or not (0)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -357,9 +408,12 @@ def main():
                      else (None, None))
     vl, vl_data = (bench_varlen(fa, torch, max(args.steps // 5, 5), min(args.warmup, 2))
                    if args.varlen else (None, None))
+    bw, bw_data = (bench_backward(fa, torch, q, k, v, tq, tk, tv, s, 3, 1) if args.backward
+                   else (None, None))
     cpu = parity = None
     if args.cpu_sample_heads > 0:
-        cpu, parity = cpu_leg((q, k, v, out_bits, s), dec_data, vl_data, args.cpu_sample_heads)
+        cpu, parity = cpu_leg((q, k, v, out_bits, s), dec_data, vl_data, args.cpu_sample_heads,
+                              bw_data)
 
     line = {
         "metric": METRIC, "value": round(value, 2), "unit": "TFLOP/s", "n_gpus": 1,
@@ -382,6 +436,7 @@ def main():
         "parity": parity,
         "decode": dec,
         "varlen": vl,
+        "backward": bw,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

@@ -335,3 +335,20 @@ def attention_bwd_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarra
             dq[b, h] = scale * (ds @ k[b, hk])
             dk[b, hk] += scale * (ds.T @ q[b, h])
     return dq, dk, dv
+
+
+def attention_bwd_dq_rows_ref(q: np.ndarray, k: np.ndarray, v: np.ndarray, do: np.ndarray,
+                              causal: bool, scale: float, b: int, h: int, rows) -> np.ndarray:
+    """dQ rows [len(rows), D] of one (b, h) by the same definition as
+    attention_bwd_ref, for sizes where the full backward is too slow: a row
+    of dQ needs only that row's P, dP and D."""
+    Hq, Sq = q.shape[1], q.shape[2]
+    Hkv, Sk = k.shape[1], k.shape[2]
+    hk = h // (Hq // Hkv)
+    rows = np.asarray(rows)
+    allowed = admissible_mask(Sq, Sk, causal, rows)
+    p = probs_ref(q[b, h, rows], k[b, hk], allowed, scale)  # [R, Sk]
+    o = p @ v[b, hk]
+    dp = do[b, h, rows] @ v[b, hk].T
+    dr = np.sum(do[b, h, rows] * o, axis=1, keepdims=True)
+    return scale * ((p * (dp - dr)) @ k[b, hk])

@@ -624,3 +624,13 @@ def test_unmutated_backward_oracle_passes_its_pin():
 @pytest.mark.parametrize("mutation", BWD_MUTATIONS, ids=[m[1][:30] for m in BWD_MUTATIONS])
 def test_planted_backward_mistake_is_caught(mutation):
     assert not _bwd_pins_pass(_mutant(*mutation))
+
+
+def test_backward_dq_rows_match_the_full_backward():
+    q, k, v, g, causal = _loss_and_grads((2, 4, 2, 9, 12, 5, True), 211)
+    dq, _, _ = oracle.attention_bwd_ref(q, k, v, g, causal, 0.5)
+    rows = [0, 3, 8]
+    for b in range(2):
+        for h in range(4):
+            got = oracle.attention_bwd_dq_rows_ref(q, k, v, g, causal, 0.5, b, h, rows)
+            np.testing.assert_allclose(got, dq[b, h, rows], atol=1e-12)
