@@ -31,17 +31,40 @@ constexpr int kBwdWaves = 4;        // waves per workgroup, 32 rows or keys each
 constexpr int kRowPad = 8;          // pad of tiles read by 16-byte row reads only
 constexpr int kTrPad = 32;          // pad of tiles that are also read transposed
 
-// Copy `valid` rows (row stride D elements in global memory) of a ROWS x D tile
-// into LDS rows of LST elements; rows past `valid` are zero.  q_sign (+1, -1,
-// 0) is applied to every element (sign bit flipped, or zeroed).
+// A ROWS x D tile in flight between global memory and LDS: each of the
+// workgroup's threads holds N of its 16-byte chunks in registers, so the next
+// tile's loads can be issued before the current tile is used.
+template <int D, int ROWS>
+struct TileRegs {
+  static constexpr int CH = D / 8;                          // chunks per row
+  static constexpr int N = ROWS * CH / (kBwdWaves * 64);    // chunks per thread
+  static_assert(ROWS * CH % (kBwdWaves * 64) == 0, "whole chunks per thread");
+  u32x4 x[N];
+};
+
+// Load `valid` rows (row stride D elements in global memory) of a tile; rows
+// past `valid` are zero.
+template <int D, int ROWS>
+__device__ __forceinline__ void fetch_tile(TileRegs<D, ROWS>& t, const uint16_t* src, int valid) {
+  using T = TileRegs<D, ROWS>;
+#pragma unroll
+  for (int i = 0; i < T::N; ++i) {
+    const int c = (int)threadIdx.x + i * kBwdWaves * 64;
+    const int r = c / T::CH, cc = c - r * T::CH;
+    t.x[i] = r < valid ? gload16(src + (long long)r * D + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+// Write a fetched tile to LDS rows of LST elements, applying q_sign (+1, -1,
+// 0: sign bit flipped, or zeroed).
 template <int D, int ROWS, int LST>
-__device__ __forceinline__ void stage_tile(uint16_t* lds, const uint16_t* src, int valid,
-                                           int q_sign) {
-  constexpr int CH = D / 8;
-  for (int c = threadIdx.x; c < ROWS * CH; c += blockDim.x) {
-    const int r = c / CH, cc = c - r * CH;
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (r < valid) x = gload16(src + (long long)r * D + cc * 8);
+__device__ __forceinline__ void store_tile(uint16_t* lds, const TileRegs<D, ROWS>& t, int q_sign) {
+  using T = TileRegs<D, ROWS>;
+#pragma unroll
+  for (int i = 0; i < T::N; ++i) {
+    const int c = (int)threadIdx.x + i * kBwdWaves * 64;
+    const int r = c / T::CH, cc = c - r * T::CH;
+    u32x4 x = t.x[i];
     if (q_sign < 0) x ^= 0x80008000u;
     if (q_sign == 0) x = u32x4{0u, 0u, 0u, 0u};
     lds_write16(lds + r * LST + cc * 8, x);
@@ -138,12 +161,22 @@ void bwd_dq_kernel(BwdParams p) {
 #pragma unroll
   for (int dt = 0; dt < DTILES; ++dt) dq[dt] = f32x16{};
 
+  // tile t + 1 is loaded into registers while tile t is used
+  TileRegs<D, BN> kt, vt;
+  if (ntiles > 0) {
+    fetch_tile(kt, kg, min(BN, Sk));
+    fetch_tile(vt, vg, min(BN, Sk));
+  }
   for (int t = 0; t < ntiles; ++t) {
     __syncthreads();  // the previous tile is no longer read
-    const int valid = min(BN, Sk - t * BN);
-    stage_tile<D, BN, KST>(Ks, kg + (long long)t * BN * D, valid, 1);
-    stage_tile<D, BN, VST>(Vs, vg + (long long)t * BN * D, valid, 1);
+    store_tile<D, BN, KST>(Ks, kt, 1);
+    store_tile<D, BN, VST>(Vs, vt, 1);
     __syncthreads();
+    if (t + 1 < ntiles) {
+      const int valid = min(BN, Sk - (t + 1) * BN);
+      fetch_tile(kt, kg + (long long)(t + 1) * BN * D, valid);
+      fetch_tile(vt, vg + (long long)(t + 1) * BN * D, valid);
+    }
     if (t * BN >= wave_end) continue;
     f32x16 S[2], dP[2];
 #pragma unroll
@@ -250,25 +283,42 @@ void bwd_dkdv_kernel(BwdParams p) {
     dv[dt] = f32x16{};
   }
 
-  // rows that see a key of this block: row + kv_off >= k0 when causal
+  // rows that see a key of this block: row + kv_off >= k0 when causal.  The
+  // steps run over (query head g of the group, 32-row tile) pairs; step it + 1
+  // is loaded into registers while step it is used.
   const int r_first = CAUSAL ? (max(0, k0 - kv_off) / BM) * BM : 0;
-  for (int g = 0; g < p.gqa; ++g) {
+  const int nrt = r_first < Sq ? (Sq - r_first + BM - 1) / BM : 0;
+  const int total = p.gqa * nrt;
+  TileRegs<D, BM> qt, gt;
+  float lnext = 0.f, dnext = 0.f;
+  auto fetch = [&](int it) {
+    const int g = it / nrt;
+    const int r0 = r_first + (it - g * nrt) * BM;
     const int hq = hk * p.gqa + g;
-    const long long qbase = ((long long)b * p.Hq + hq) * Sq * D;
+    const long long qbase = ((long long)b * p.Hq + hq) * Sq * D + (long long)r0 * D;
     const long long sbase = ((long long)b * p.Hq + hq) * Sq;
-    for (int r0 = r_first; r0 < Sq; r0 += BM) {
+    const int valid = min(BM, Sq - r0);
+    fetch_tile(qt, static_cast<const uint16_t*>(p.q) + qbase, valid);
+    fetch_tile(gt, static_cast<const uint16_t*>(p.dout) + qbase, valid);
+    if (tid < BM) {
+      const int r = r0 + tid;
+      lnext = r < Sq ? p.lse[sbase + r] * kLog2e : 0.f;
+      dnext = r < Sq ? p.dsum[sbase + r] : 0.f;
+    }
+  };
+  if (total > 0) fetch(0);
+  for (int it = 0; it < total; ++it) {
+    {
+      const int r0 = r_first + (it % nrt) * BM;
       __syncthreads();  // the previous tile is no longer read
-      const int valid = min(BM, Sq - r0);
-      stage_tile<D, BM, QST>(Qs, static_cast<const uint16_t*>(p.q) + qbase + (long long)r0 * D,
-                             valid, p.q_sign);
-      stage_tile<D, BM, QST>(Gs, static_cast<const uint16_t*>(p.dout) + qbase + (long long)r0 * D,
-                             valid, 1);
+      store_tile<D, BM, QST>(Qs, qt, p.q_sign);
+      store_tile<D, BM, QST>(Gs, gt, 1);
       if (tid < BM) {
-        const int r = r0 + tid;
-        Ls[tid] = r < Sq ? p.lse[sbase + r] * kLog2e : 0.f;
-        Ds[tid] = r < Sq ? p.dsum[sbase + r] : 0.f;
+        Ls[tid] = lnext;
+        Ds[tid] = dnext;
       }
       __syncthreads();
+      if (it + 1 < total) fetch(it + 1);
       if (kw0 >= Sk) continue;                            // no keys in this wave
       if (CAUSAL && kw0 > r0 + BM - 1 + kv_off) continue;  // every pair masked
       f32x16 S = f32x16{}, dP = f32x16{};
