@@ -8,7 +8,7 @@
 //   dq    per 128 query rows: S^T = K Q^T, dP^T = V dO^T,
 //         P = exp2(S c - LSE_i log2 e), dS = P (dP - D_i),
 //         dQ^T += K^T dS^T                       (Q and dO stay in registers)
-//   dkdv  per 128 keys: S = Q K^T, dP = dO V^T, P and dS as above,
+//   dkdv  per 128 keys, 64 query rows a step: S = Q K^T, dP = dO V^T, P and dS as above,
 //         dV^T += dO^T P, dK^T += Q^T dS   (K and V stay in registers; the
 //         query heads of a GQA group add into their kv head in the loop, so
 //         no atomics are needed anywhere)
@@ -241,7 +241,7 @@ template <int D, int DT, bool CAUSAL>
 __global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams p) {
   using E = Elt<DT>;
-  constexpr int BM = 32;                 // query rows per step
+  constexpr int BM = 64;                 // query rows per step (two 32-row sub-tiles)
   constexpr int KSTEPS = D / 16, DTILES = D / 32;
   constexpr int QST = D + kTrPad;        // Q and dO: row reads and transposed reads
   __shared__ __attribute__((aligned(16))) uint16_t Qs[BM * QST];
@@ -321,42 +321,52 @@ void bwd_dkdv_kernel(BwdParams p) {
       if (it + 1 < total) fetch(it + 1);
       if (kw0 >= Sk) continue;                            // no keys in this wave
       if (CAUSAL && kw0 > r0 + BM - 1 + kv_off) continue;  // every pair masked
-      f32x16 S = f32x16{}, dP = f32x16{};
+      f32x16 S[2], dP[2];
 #pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        S = E::mfma(lds_read16(Qs + li * QST + 16 * kk + 8 * lh), kr[kk], S);
-        dP = E::mfma(lds_read16(Gs + li * QST + 16 * kk + 8 * lh), vr[kk], dP);
+      for (int st = 0; st < 2; ++st) {
+        S[st] = f32x16{};
+        dP[st] = f32x16{};
+#pragma unroll
+        for (int kk = 0; kk < KSTEPS; ++kk) {
+          S[st] = E::mfma(lds_read16(Qs + (32 * st + li) * QST + 16 * kk + 8 * lh), kr[kk], S[st]);
+          dP[st] = E::mfma(lds_read16(Gs + (32 * st + li) * QST + 16 * kk + 8 * lh), vr[kk], dP[st]);
+        }
       }
-      // lane = key; register r is query row r0 + 8 (r/4) + 4 lh + r%4
+      // lane = key; register r of sub-tile st is query row r0 + 32 st + 8 (r/4) + 4 lh + r%4
+      u32x4 pb[2][2], db[2][2];
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int rr = 8 * (r >> 2) + 4 * lh + (r & 3);
-        const int rowi = r0 + rr;
-        const bool ok = rowi < Sq && key < Sk && (!CAUSAL || key <= rowi + kv_off);
-        const float pr = ok ? fast_exp2(__builtin_fmaf(S[r], c, -Ls[rr])) : 0.f;
-        S[r] = pr;
-        dP[r] = pr * (dP[r] - Ds[rr]);
-      }
-      u32x4 pb[2], db[2];
+      for (int st = 0; st < 2; ++st) {
 #pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int q = 8 * kk;
-        pb[kk] = u32x4{E::pack2(S[q + 0], S[q + 1]), E::pack2(S[q + 2], S[q + 3]),
-                       E::pack2(S[q + 4], S[q + 5]), E::pack2(S[q + 6], S[q + 7])};
-        db[kk] = u32x4{E::pack2(dP[q + 0], dP[q + 1]), E::pack2(dP[q + 2], dP[q + 3]),
-                       E::pack2(dP[q + 4], dP[q + 5]), E::pack2(dP[q + 6], dP[q + 7])};
+        for (int r = 0; r < 16; ++r) {
+          const int rr = 32 * st + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const int rowi = r0 + rr;
+          const bool ok = rowi < Sq && key < Sk && (!CAUSAL || key <= rowi + kv_off);
+          const float pr = ok ? fast_exp2(__builtin_fmaf(S[st][r], c, -Ls[rr])) : 0.f;
+          S[st][r] = pr;
+          dP[st][r] = pr * (dP[st][r] - Ds[rr]);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int q = 8 * kk;
+          pb[st][kk] = u32x4{E::pack2(S[st][q + 0], S[st][q + 1]), E::pack2(S[st][q + 2], S[st][q + 3]),
+                             E::pack2(S[st][q + 4], S[st][q + 5]), E::pack2(S[st][q + 6], S[st][q + 7])};
+          db[st][kk] = u32x4{E::pack2(dP[st][q + 0], dP[st][q + 1]), E::pack2(dP[st][q + 2], dP[st][q + 3]),
+                             E::pack2(dP[st][q + 4], dP[st][q + 5]), E::pack2(dP[st][q + 6], dP[st][q + 7])};
+        }
       }
       // dV^T += dO^T P and dK^T += Q^T dS: dO^T, Q^T by transposing reads,
       // rows in the register order of P and dS
 #pragma unroll
+      for (int st = 0; st < 2; ++st)
+#pragma unroll
       for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
         for (int dt = 0; dt < DTILES; ++dt) {
-          const int off = v_lane + 16 * kk * QST + 32 * dt;
+          const int off = v_lane + (32 * st + 16 * kk) * QST + 32 * dt;
           const u32x2 glo = lds_read_tr16(Gs + off), ghi = lds_read_tr16(Gs + off + 8 * QST);
-          dv[dt] = E::mfma(u32x4{glo[0], glo[1], ghi[0], ghi[1]}, pb[kk], dv[dt]);
+          dv[dt] = E::mfma(u32x4{glo[0], glo[1], ghi[0], ghi[1]}, pb[st][kk], dv[dt]);
           const u32x2 qlo = lds_read_tr16(Qs + off), qhi = lds_read_tr16(Qs + off + 8 * QST);
-          dk[dt] = E::mfma(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, db[kk], dk[dt]);
+          dk[dt] = E::mfma(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, db[st][kk], dk[dt]);
         }
     }
   }
