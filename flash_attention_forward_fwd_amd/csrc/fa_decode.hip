@@ -43,6 +43,11 @@ constexpr int kMergeGroup = 16;  // partials merged by one workgroup
 #endif
 constexpr bool kMergeKernel = FA_DECODE_MERGE_KERNEL != 0;
 constexpr int kDVPad = 32;       // V staging row pad (elements)
+// 32-token chunks per split at full capacity
+#ifndef FA_DECODE_CHUNKS_PER_SPLIT
+#define FA_DECODE_CHUNKS_PER_SPLIT 8
+#endif
+constexpr int kChunksPerSplit = FA_DECODE_CHUNKS_PER_SPLIT;
 
 // Query heads of head group hg (groups of hpg heads of one kv head's gqa).
 __device__ __forceinline__ int heads_in_group(int hpg, int gqa, int hg) {
@@ -663,11 +668,11 @@ hipError_t launch_p(const DecodeParams& p, hipStream_t stream) {
 }  // namespace
 
 int decode_num_splits(int B, int Hkv, int capacity) {
-  // about 256 tokens (8 chunks of 32) per split at full capacity, and at
+  // about kChunksPerSplit (8: 256 tokens) chunks per split at full capacity, and at
   // most 256 splits per (batch, kv head): 64 MiB of K+V over 512 workgroups
   // at the largest cache of the decode workload
   const int chunks = (capacity + 31) / 32;
-  int ns = (chunks + 7) / 8;
+  int ns = (chunks + kChunksPerSplit - 1) / kChunksPerSplit;
   if (ns > 256) ns = 256;
   if (ns < 1) ns = 1;
   (void)B;
