@@ -542,21 +542,39 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
                              scratch);
 }
 
+// Reduction over the lanes of a wave that differ in lane bits 3..5 (lane % 8
+// fixed), every lane receiving the result, on the vector unit: a DPP rotate
+// of the 16-lane row by 8 (lane ^ 8), then the gfx950 swaps of 16-lane rows
+// (lane ^ 16) and 32-lane halves (lane ^ 32).  Each step combines a lane with
+// its partner symmetrically, so all lanes of a group hold the same bits.
+template <class Op>
+__device__ __forceinline__ float reduce_lane_bits345(float x, Op op) {
+  x = op(x, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), 0x128 /* row_ror:8 */,
+                                                       0xF, 0xF, false)));
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  x = op(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  const auto h = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return op(__uint_as_float(h[0]), __uint_as_float(h[1]));
+}
+
 // Second kernel: merges the nsplit (<= 256, see decode_num_splits) split
 // records of (unit, column g = (query token, head) of the group) for 32
-// columns of O.  Thread t takes
-// columns 4 (t % 8) .. + 3 of records s = t / 8 + 32 k.  The kernel boundary
-// makes the records visible, so plain loads suffice; they do not depend on
-// the merge weights, so they are issued first, together with the (m, l)
-// loads, and the whole merge costs one memory round trip.
+// columns of O.  Thread t takes columns 4 (t % 8) .. + 3 of records
+// s = t / 8 + 32 k, k < 8, together with those records' (m, l).  The kernel
+// boundary makes the records visible, so plain loads suffice, and all of
+// them are issued before any is used: the merge costs one memory round trip,
+// two lane reductions and two barriers (the maximum M over the records, then
+// the weighted sums).
 constexpr int kMergeThreads = 256;
 template <int D, int DT>
 __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParams p) {
   using E = Elt<DT>;
   constexpr int NW = kMergeThreads / 64;
-  __shared__ float w[256];
-  __shared__ float red[NW][2];
+  __shared__ float red_m[NW];
   __shared__ f32x4 part[NW][8];
+  __shared__ float part_l[NW][8];
   const int unit = blockIdx.x, g = blockIdx.y, col0 = 32 * blockIdx.z;  // g: record column
   const int HG = (p.gqa + p.hpg - 1) / p.hpg;
   const int hg = unit % HG;
@@ -571,58 +589,66 @@ __global__ __launch_bounds__(kMergeThreads) void decode_merge_kernel(DecodeParam
   const int t = threadIdx.x, lane = t & 63, wv = t >> 6;
   const int cg = t & 7, rl = t >> 3;
   const float* po = p.part_o + (rec0 * cs + g) * D + col0 + 4 * cg;
+  const float* pml = p.part_ml + (rec0 * cs + g) * 2;
   f32x4 x[8];
+  f32x2 ml[8];
+  // loads without branches: records past ns read record 0 (always written)
+  // and are then replaced by an empty record (m = -inf, l = 0, acc = 0)
 #pragma unroll
   for (int k = 0; k < 8; ++k) {
     const int s = rl + 32 * k;
-    x[k] = s < ns ? *reinterpret_cast<const f32x4*>(po + (long long)s * cs * D) : f32x4{0.f, 0.f, 0.f, 0.f};
+    const int sc = s < ns ? s : 0;
+    x[k] = *reinterpret_cast<const f32x4*>(po + (long long)sc * cs * D);
+    ml[k] = *reinterpret_cast<const f32x2*>(pml + (long long)sc * cs * 2);
   }
-  // weights: M = max_s m_s, w_s = 2^(m_s - M), den = sum_s w_s l_s
-  float m = -__builtin_inff(), l = 0.f;
-  if (t < ns) {
-    const f32x2 ml = *reinterpret_cast<const f32x2*>(p.part_ml + ((rec0 + t) * cs + g) * 2);
-    m = ml[0];
-    l = ml[1];
-  }
-  float M = m;
+  __builtin_amdgcn_sched_barrier(0);  // every load is issued before any is used
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
-  if (lane == 0) red[wv][0] = M;
+  for (int k = 0; k < 8; ++k) {
+    const bool in = rl + 32 * k < ns;
+    ml[k][0] = in ? ml[k][0] : -__builtin_inff();
+  }
+  // M = max_s m_s over all records
+  float M = ml[0][0];
+#pragma unroll
+  for (int k = 1; k < 8; ++k) M = fmaxf(M, ml[k][0]);
+  M = reduce_lane_bits345(M, [](float a, float c) { return fmaxf(a, c); });
+  if (lane == 0) red_m[wv] = M;
   __syncthreads();
-  M = red[0][0];
+  M = red_m[0];
 #pragma unroll
-  for (int i = 1; i < NW; ++i) M = fmaxf(M, red[i][0]);
+  for (int i = 1; i < NW; ++i) M = fmaxf(M, red_m[i]);
+  // weights w_s = 2^(m_s - M); sum_s w_s acc_s and sum_s w_s l_s
   const float Mu = (M == -__builtin_inff()) ? 0.f : M;
-  const float f = t < ns ? fast_exp2(m - Mu) : 0.f;  // m = -inf -> 0
-  w[t] = f;
-  float dl = f * l;
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) dl += __shfl_xor(dl, o);
-  if (lane == 0) red[wv][1] = dl;
-  __syncthreads();
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   float den = 0.f;
 #pragma unroll
-  for (int i = 0; i < NW; ++i) den += red[i][1];
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
   for (int k = 0; k < 8; ++k) {
-    const int s = rl + 32 * k;
-    if (s < ns && w[s] != 0.f) acc += w[s] * x[k];
-  }
-  // sum over the records: lanes of one column group inside a wave (lane % 8
-  // equal), then the waves
+    // a record of weight 0 (an empty split, or past ns) adds nothing, its
+    // contents unread
+    const float w = fast_exp2(ml[k][0] - Mu);  // m = -inf -> 0
+    const bool use = w != 0.f;
 #pragma unroll
-  for (int o = 8; o < 64; o <<= 1) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += __shfl_xor(acc[i], o);
+    for (int i = 0; i < 4; ++i) acc[i] = __builtin_fmaf(w, use ? x[k][i] : 0.f, acc[i]);
+    den = __builtin_fmaf(w, use ? ml[k][1] : 0.f, den);
   }
-  if (lane < 8) part[wv][lane] = acc;
+  auto add = [](float a, float c) { return a + c; };
+#pragma unroll
+  for (int i = 0; i < 4; ++i) acc[i] = reduce_lane_bits345(acc[i], add);
+  den = reduce_lane_bits345(den, add);
+  if (lane < 8) {
+    part[wv][lane] = acc;
+    part_l[wv][lane] = den;
+  }
   __syncthreads();
   if (t < 8) {
     f32x4 sum = part[0][t];
+    float dsum = part_l[0][t];
 #pragma unroll
-    for (int i = 1; i < NW; ++i) sum += part[i][t];
-    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    for (int i = 1; i < NW; ++i) {
+      sum += part[i][t];
+      dsum += part_l[i][t];
+    }
+    const float inv = dsum > 0.f ? 1.0f / dsum : 0.f;
     const u32x2 pk = {E::pack2(sum[0] * inv, sum[1] * inv), E::pack2(sum[2] * inv, sum[3] * inv)};
     uint16_t* og = static_cast<uint16_t*>(p.o);
     const int qt = g / gh;                              // query token of the column
