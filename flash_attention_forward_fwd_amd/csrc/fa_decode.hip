@@ -274,14 +274,45 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
   const int cstride = min(hpg, p.gqa) * sq;     // columns per record
   const int hq0 = hk * p.gqa + hpg * hg;  // first query head of this group
 
+  // Q of the group's heads (lane: column li, d = 16kk + 8lh + e) does not
+  // depend on the valid length: its loads are issued first, without
+  // branches (columns past gg read column 0 and are zeroed below), so their
+  // round trip overlaps the valid-length read and the compiler can count
+  // them exactly when it later waits for them
+  const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(p.q);
+  u32x4 qr[KSTEPS];
+  {
+    const int col = li < gg ? li : 0;
+    const int t = MULTI ? col / gh : 0;
+    const uint16_t* qrow = qg + (((long long)b * sq + t) * p.Hq + hq0 + col - t * gh) * D + 8 * lh;
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk) qr[kk] = gload16(qrow + 16 * kk);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
   int L = p.valid_len[b];
   L = min(max(L, 0), p.capacity);
+
+  // Q as the B operand: columns past the group's gg are zero, and the sign
+  // of the scale is applied to Q (q_sign -1: negated, 0: zero), so the
+  // scores' scale factor c is never negative.  The empty asm pins the
+  // result here, ahead of every K/V load: computed later (where the
+  // compiler would sink it), its wait for Q would also wait for the first
+  // chunk's loads.
+#pragma unroll
+  for (int kk = 0; kk < KSTEPS; ++kk) {
+    u32x4 x = qr[kk];
+    x = p.q_sign < 0 ? (x ^ 0x80008000u) : x;
+    qr[kk] = (li < gg && p.q_sign != 0) ? x : u32x4{0u, 0u, 0u, 0u};
+#if defined(__HIP_DEVICE_COMPILE__)
+    asm volatile("" : "+v"(qr[kk]));
+#endif
+  }
   const int nchunks = (L + 31) / 32;
   const int cps = (nchunks + p.nsplit - 1) / p.nsplit;  // chunks per split
   const int c0 = min(split * cps, nchunks);
   const int c1 = min(c0 + cps, nchunks);
 
-  const uint16_t* __restrict__ qg = static_cast<const uint16_t*>(p.q);
   const uint16_t* __restrict__ kg = static_cast<const uint16_t*>(p.k);
   const uint16_t* __restrict__ vg = static_cast<const uint16_t*>(p.v);
   const float c = p.c_log2;
@@ -304,19 +335,6 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     }
   }
 
-  // Q of the group's heads as the B operand (lane: head li, d = 16kk + 8lh + e)
-  u32x4 qr[KSTEPS];
-#pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) {
-    u32x4 x = {0u, 0u, 0u, 0u};
-    if (li < gg) {
-      const int t = MULTI ? li / gh : 0;
-      x = gload16(qg + (((long long)b * sq + t) * p.Hq + hq0 + li - t * gh) * D + 16 * kk + 8 * lh);
-    }
-    if (p.q_sign < 0) x ^= 0x80008000u;
-    if (p.q_sign == 0) x = u32x4{0u, 0u, 0u, 0u};
-    qr[kk] = x;
-  }
 
   // K and V of this (batch, kv head) as buffer ranges that end at token L:
   // token j's row sits at byte j * tok_stride * 2, and rows at or past L read
