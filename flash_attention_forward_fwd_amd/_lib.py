@@ -51,7 +51,8 @@ class FwdPlan(ctypes.Structure):
     _fields_ = [("block_m", ctypes.c_int), ("block_n", ctypes.c_int),
                 ("work_items", ctypes.c_int), ("grid", ctypes.c_int),
                 ("persistent", ctypes.c_int), ("hkv_major", ctypes.c_int),
-                ("kv_tiles", ctypes.c_longlong), ("masked_tiles", ctypes.c_longlong)]
+                ("kv_tiles", ctypes.c_longlong), ("masked_tiles", ctypes.c_longlong),
+                ("xcd_map", ctypes.c_int)]
 
 
 _lib = None

@@ -82,9 +82,21 @@ fa_status_t plan_prefill(int B, int Hq, int Hkv, int Sq, int Sk, int D, int caus
   // kv-head-major order when GQA and gqa*NQB*B >= 2*NP, else query-block-major
   const long long gqa = Hq / Hkv;
   int hkv = (persistent && gqa > 1 && gqa * nqb * B >= 2LL * NP) ? 1 : 0;
+  // XCD-aware dealing of the (batch, kv head) units, possible when the
+  // persistent grid and the unit count both split evenly over the XCDs (every
+  // XCD then holds the same multiset of items).  Chosen where the order is
+  // query-block-major: each round then spans every unit, and without the
+  // dealing every XCD's L2 would fetch the K/V of all of them.  Kv-head-major
+  // rounds already span one or two kv heads.
+  const bool xcd_ok = persistent && plan->grid == NP && NP % fa::kXcds == 0 &&
+                      ((long long)B * Hkv) % fa::kXcds == 0;
+  int xcd = (xcd_ok && !hkv) ? 1 : 0;
   const int eo = env_choice("FA_PREFILL_ORDER");
   if (eo >= 0) hkv = eo;
+  const int ex = env_choice("FA_PREFILL_XCD");
+  if (ex >= 0) xcd = xcd_ok ? ex : 0;
   plan->hkv_major = hkv;
+  plan->xcd_map = xcd;
   // tiles streamed and tiles needing the mask, per query block (x Hq*B)
   long long tiles = 0, masked = 0;
   const long long off = (long long)Sk - Sq;
@@ -160,6 +172,7 @@ fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
   p.work_items = plan.work_items;
   p.hkv_major = plan.hkv_major;
   p.persistent = plan.persistent;
+  p.xcd_map = plan.xcd_map;
   fold_scale(scale, &p.c_log2, &p.q_sign);
   const hipError_t e = fa::launch_prefill(p, D, dtype, causal != 0, plan.grid,
                                           static_cast<hipStream_t>(stream));
@@ -232,6 +245,7 @@ fa_status_t launch_varlen(const void* q, const void* k, const void* v, void* o, 
   p.work_items = plan.work_items;
   p.hkv_major = plan.hkv_major;
   p.persistent = plan.persistent;
+  p.xcd_map = 0;  // the varlen list is dealt by its own compacted order
   fold_scale(scale, &p.c_log2, &p.q_sign);
   const hipError_t e = fa::launch_prefill(p, D, dtype, causal != 0, plan.grid,
                                           static_cast<hipStream_t>(stream));

@@ -21,6 +21,9 @@ constexpr int kNumCUs = 256;                     // MI355X compute units
 // two waves per SIMD: 8 waves per CU
 constexpr int kPrefillCTAsPerCU = 8 / kPrefillWaves;
 constexpr int kPersistentCTAs = kNumCUs * kPrefillCTAsPerCU;
+// MI355X accelerator dies (XCDs), each with its own L2; workgroup i of a
+// launch is dispatched to XCD i % kXcds
+constexpr int kXcds = 8;
 
 struct PrefillParams {
   const void* q;
@@ -42,6 +45,12 @@ struct PrefillParams {
   int work_items;      // nqb * Hq * B
   int hkv_major;       // work-item order
   int persistent;      // grid-stride over work items
+  // 1: the B * Hkv (batch, kv head) units are dealt to the XCDs (unit u to
+  // XCD u % kXcds) and each XCD's workgroups stride over its own units'
+  // items, so a kv head's K/V tiles are fetched into one L2 only.  Needs a
+  // persistent grid of a multiple of kXcds workgroups and B * Hkv a multiple
+  // of kXcds; hkv_major then orders each XCD's list unit-major.
+  int xcd_map;
   float c_log2;        // |scale| * log2(e), or 1 when scale == 0
   int q_sign;          // +1, -1, or 0 (scale == 0): applied to q in registers
 };

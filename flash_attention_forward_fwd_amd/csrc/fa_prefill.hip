@@ -129,6 +129,34 @@ __device__ __forceinline__ void decode_item(const PrefillParams& p, int w, int& 
   }
 }
 
+// Item w of XCD x's list -> (batch, query head, query block).  The XCD owns
+// the units u = (batch, kv head) = b * Hkv + hk with u % kXcds == x, its
+// ui-th unit being ui * kXcds + x.  Its list runs unit-major (unit, query
+// block descending, group member) when hkv_major, else block-major (query
+// block descending, unit, group member).
+__device__ __forceinline__ void xcd_item(const PrefillParams& p, int x, int w, int& b, int& hq,
+                                         int& qb) {
+  const int nu = p.B * p.Hkv / kXcds;  // units per XCD
+  int ui, lvl;
+  if (p.hkv_major) {
+    const int per_unit = p.gqa * p.nqb;
+    ui = w / per_unit;
+    const int r = w - ui * per_unit;
+    lvl = r / p.gqa;
+    w = r - lvl * p.gqa;
+  } else {
+    const int per_lvl = nu * p.gqa;
+    lvl = w / per_lvl;
+    const int r = w - lvl * per_lvl;
+    ui = r / p.gqa;
+    w = r - ui * p.gqa;
+  }
+  const int u = ui * kXcds + x;
+  b = u / p.Hkv;
+  hq = (u - b * p.Hkv) * p.gqa + w;
+  qb = p.nqb - 1 - lvl;
+}
+
 // Packed varlen schedule.  The work items are the non-empty (sequence, query
 // head, query block) triples, in the dense order: block level descending (a
 // causal block's cost grows with its index whatever sequence it belongs to),
@@ -247,15 +275,22 @@ void prefill_kernel(PrefillParams p) {
     }
   }
 
-  const int NP = gridDim.x;
+  // The workgroups that stride over one item list: the whole grid, or with
+  // the XCD map the grid's workgroups on one XCD (workgroup i runs on XCD
+  // i % kXcds), which stride over the items of that XCD's units only.
+  const bool xmap = !VARLEN && p.xcd_map;
+  const int xcd = xmap ? (int)blockIdx.x % kXcds : 0;
+  const int NP = xmap ? (int)gridDim.x / kXcds : (int)gridDim.x;
+  const int cta = xmap ? (int)blockIdx.x / kXcds : (int)blockIdx.x;
+  const int list_items = xmap ? work_items / kXcds : work_items;
   for (int round = 0;; ++round) {
     int w;
     if (p.persistent) {
-      if (round * NP >= work_items) break;
+      if (round * NP >= list_items) break;
       // snake order: even rounds ascend, odd rounds descend, so every CTA
       // pairs a heavy item with a light one
-      w = round * NP + ((round & 1) ? (NP - 1 - (int)blockIdx.x) : (int)blockIdx.x);
-      if (w >= work_items) continue;
+      w = round * NP + ((round & 1) ? (NP - 1 - cta) : cta);
+      if (w >= list_items) continue;
     } else {
       if (round > 0) break;
       w = blockIdx.x;
@@ -263,6 +298,7 @@ void prefill_kernel(PrefillParams p) {
     }
     int b, hq, qb;
     if (compact) varlen_item(p, nqb_tab, total_blocks, w, lane, b, hq, qb);
+    else if (xmap) xcd_item(p, xcd, w, b, hq, qb);
     else decode_item(p, w, b, hq, qb);
     const int hk = hq / p.gqa;
     const int q0 = qb * BM;

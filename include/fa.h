@@ -139,6 +139,11 @@ typedef struct {
   int hkv_major;        /* 1 = work items ordered kv-head-major, 0 = query-block-major */
   long long kv_tiles;   /* KV tiles streamed, summed over work items */
   long long masked_tiles; /* of those, tiles that need the mask */
+  int xcd_map;          /* 1 = each XCD's workgroups take the items of the
+                           (batch, kv head) units u with u % 8 == XCD, so a kv
+                           head's K/V is fetched into one XCD's L2 only; chosen
+                           for query-block-major persistent launches whose unit
+                           count B * Hkv is a multiple of 8 */
 } fa_fwd_plan_t;
 
 fa_status_t fa_fwd_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,

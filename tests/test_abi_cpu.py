@@ -263,6 +263,13 @@ def test_work_items_and_orders():
     for c in FACTS["hkv_major_rule"]["cases"]:
         p = fa.fwd_plan(c["B"], c["Hq"], c["Hkv"], c["Sq"], c["Sq"], 128, True)
         assert p["hkv_major"] == (c["order"] == "hkv_major"), c
+    # XCD dealing: on for query-block-major persistent launches when the
+    # B * Hkv units split over the 8 XCDs
+    assert fa.fwd_plan(1, 128, 8, 8192, 8192, 128, True)["xcd_map"] == 0  # kv-head-major
+    assert fa.fwd_plan(4, 32, 8, 4096, 4096, 128, True)["xcd_map"] == 1
+    assert fa.fwd_plan(4, 32, 8, 1000, 3000, 128, True)["xcd_map"] == 1
+    assert fa.fwd_plan(1, 32, 4, 4096, 4096, 128, True)["xcd_map"] == 0   # 4 units
+    assert fa.fwd_plan(1, 16, 16, 2048, 2048, 128, True)["xcd_map"] == 0  # not persistent
     for c in FACTS["persistent_auto"]["cases"]:
         p = fa.fwd_plan(c["B"], c["Hq"], c["Hq"], c["Sq"], c["Sq"], 128, True)
         assert p["persistent"] == int(c["persistent"]), c

@@ -297,12 +297,18 @@ def test_guard_bands_untouched_and_unread():
 
 def test_persistent_and_grid_launches_agree_bitwise(monkeypatch):
     # the same items computed by the persistent grid-stride launch, in both
-    # orders, and by one workgroup per item give identical bits
+    # orders, with and without the XCD dealing of (batch, kv head) units, and
+    # by one workgroup per item give identical bits
     dtype = "bf16"
-    q, k, v = shape_inputs(1, 32, 4, 1024, 1024, 128, dtype, seed=106)
+    B, Hq, Hkv, S = 2, 32, 4, 1024
+    assert _fa().fwd_plan(B, Hq, Hkv, S, S, 128, True)["xcd_map"] == 1
+    q, k, v = shape_inputs(B, Hq, Hkv, S, S, 128, dtype, seed=106)
     outs = []
-    for pers, order in (("off", "qb"), ("on", "qb"), ("on", "hkv")):
+    for pers, order, xcd in (("off", "qb", "off"), ("on", "qb", "off"), ("on", "hkv", "off"),
+                             ("on", "qb", "on"), ("on", "hkv", "on")):
         monkeypatch.setenv("FA_PREFILL_PERSISTENT", pers)
         monkeypatch.setenv("FA_PREFILL_ORDER", order)
+        monkeypatch.setenv("FA_PREFILL_XCD", xcd)
         outs.append(run_fwd(q, k, v, True, 0.088, dtype))
-    assert np.array_equal(outs[0], outs[1]) and np.array_equal(outs[0], outs[2])
+    for o in outs[1:]:
+        assert np.array_equal(outs[0], o)
