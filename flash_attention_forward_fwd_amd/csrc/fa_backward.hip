@@ -30,6 +30,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBwdWaves = 4;        // waves per workgroup, 32 rows or keys each
 constexpr int kRowPad = 8;          // pad of tiles read by 16-byte row reads only
 constexpr int kTrPad = 32;          // pad of tiles that are also read transposed
+constexpr int kPipe = 4;            // MFMAs an LDS operand read runs ahead of its use
 
 // A ROWS x D tile in flight between global memory and LDS: each of the
 // workgroup's threads holds N of its 16-byte chunks in registers, so the next
@@ -178,16 +179,21 @@ void bwd_dq_kernel(BwdParams p) {
       fetch_tile(vt, vg + (long long)(t + 1) * BN * D, valid);
     }
     if (t * BN >= wave_end) continue;
+    // S^T = K Q^T and dP^T = V dO^T, the two products' MFMAs alternating,
+    // each LDS operand read kPipe MFMAs ahead
     f32x16 S[2], dP[2];
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      S[st] = f32x16{};
-      dP[st] = f32x16{};
-#pragma unroll
-      for (int kk = 0; kk < KSTEPS; ++kk) {
-        S[st] = E::mfma(lds_read16(Ks + (32 * st + li) * KST + 16 * kk + 8 * lh), qr[kk], S[st]);
-        dP[st] = E::mfma(lds_read16(Vs + (32 * st + li) * VST + 16 * kk + 8 * lh), gr[kk], dP[st]);
-      }
+    {
+      auto load = [&](auto jc) -> u32x4 {
+        constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
+        if constexpr (j % 2) return lds_read16(Vs + (32 * st + li) * VST + 16 * kk + 8 * lh);
+        else return lds_read16(Ks + (32 * st + li) * KST + 16 * kk + 8 * lh);
+      };
+      auto mfma = [&](auto jc, u32x4 a) {
+        constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
+        if constexpr (j % 2) dP[st] = E::mfma(a, gr[kk], kk == 0 ? f32x16{} : dP[st]);
+        else S[st] = E::mfma(a, qr[kk], kk == 0 ? f32x16{} : S[st]);
+      };
+      m_pipeline<4 * KSTEPS, kPipe>(load, mfma);
     }
     // lane = query row; register r of sub-tile st is key t*BN + 32 st + 8 (r/4) + 4 lh + r%4
     u32x4 db[2][2];
@@ -207,18 +213,23 @@ void bwd_dq_kernel(BwdParams p) {
                            E::pack2(S[st][r0 + 4], S[st][r0 + 5]), E::pack2(S[st][r0 + 6], S[st][r0 + 7])};
       }
     }
-    // dQ^T += K^T dS^T: K^T by transposing reads, keys in dS's register order
-#pragma unroll
-    for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int dt = 0; dt < DTILES; ++dt) {
-          const uint16_t* kr = Ks + v_lane + (32 * st + 16 * kk) * KST + 32 * dt;
-          const u32x2 lo = lds_read_tr16(kr);
-          const u32x2 hi = lds_read_tr16(kr + 8 * KST);
-          dq[dt] = E::mfma(u32x4{lo[0], lo[1], hi[0], hi[1]}, db[st][kk], dq[dt]);
-        }
+    // dQ^T += K^T dS^T: K^T by transposing reads, keys in dS's register
+    // order; MFMA j = (sub-tile st, k-step kk, column tile dt)
+    {
+      auto load = [&](auto jc) -> u32x4 {
+        constexpr int j = decltype(jc)::value, dt = j % DTILES, kk = (j / DTILES) % 2;
+        constexpr int st = j / (2 * DTILES);
+        const uint16_t* kr = Ks + v_lane + (32 * st + 16 * kk) * KST + 32 * dt;
+        const u32x2 lo = lds_read_tr16(kr), hi = lds_read_tr16(kr + 8 * KST);
+        return u32x4{lo[0], lo[1], hi[0], hi[1]};
+      };
+      auto mfma = [&](auto jc, u32x4 a) {
+        constexpr int j = decltype(jc)::value, dt = j % DTILES, kk = (j / DTILES) % 2;
+        constexpr int st = j / (2 * DTILES);
+        dq[dt] = E::mfma(a, db[st][kk], dq[dt]);
+      };
+      m_pipeline<4 * DTILES, kPipe>(load, mfma);
+    }
   }
 
   // dQ = scale * (dS K): lane row li, d = 32 dt + 8 (r/4) + 4 lh + r%4
@@ -246,7 +257,8 @@ void bwd_dkdv_kernel(BwdParams p) {
   constexpr int QST = D + kTrPad;        // Q and dO: row reads and transposed reads
   __shared__ __attribute__((aligned(16))) uint16_t Qs[BM * QST];
   __shared__ __attribute__((aligned(16))) uint16_t Gs[BM * QST];
-  __shared__ float Ls[BM], Ds[BM];
+  __shared__ __attribute__((aligned(16))) float Ls[BM];
+  __shared__ __attribute__((aligned(16))) float Ds[BM];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
@@ -321,29 +333,45 @@ void bwd_dkdv_kernel(BwdParams p) {
       if (it + 1 < total) fetch(it + 1);
       if (kw0 >= Sk) continue;                            // no keys in this wave
       if (CAUSAL && kw0 > r0 + BM - 1 + kv_off) continue;  // every pair masked
+      // S = Q K^T and dP = dO V^T, the two products' MFMAs alternating, each
+      // LDS operand read kPipe MFMAs ahead (one wave per SIMD: nothing else
+      // hides the LDS latency)
       f32x16 S[2], dP[2];
-#pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        S[st] = f32x16{};
-        dP[st] = f32x16{};
-#pragma unroll
-        for (int kk = 0; kk < KSTEPS; ++kk) {
-          S[st] = E::mfma(lds_read16(Qs + (32 * st + li) * QST + 16 * kk + 8 * lh), kr[kk], S[st]);
-          dP[st] = E::mfma(lds_read16(Gs + (32 * st + li) * QST + 16 * kk + 8 * lh), vr[kk], dP[st]);
-        }
+      {
+        auto load = [&](auto jc) -> u32x4 {
+          constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
+          const uint16_t* src = (j % 2) ? Gs : Qs;
+          return lds_read16(src + (32 * st + li) * QST + 16 * kk + 8 * lh);
+        };
+        auto mfma = [&](auto jc, u32x4 a) {
+          constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
+          if constexpr (j % 2) dP[st] = E::mfma(a, vr[kk], kk == 0 ? f32x16{} : dP[st]);
+          else S[st] = E::mfma(a, kr[kk], kk == 0 ? f32x16{} : S[st]);
+        };
+        m_pipeline<4 * KSTEPS, kPipe>(load, mfma);
       }
       // lane = key; register r of sub-tile st is query row r0 + 32 st + 8 (r/4) + 4 lh + r%4
       u32x4 pb[2][2], db[2][2];
 #pragma unroll
       for (int st = 0; st < 2; ++st) {
+        // the rows' LSE and D, four consecutive rows per 16-byte read, read
+        // before any is used; every exp2 is evaluated and masked pairs are
+        // then selected to 0, so the loop has no branch
+        f32x4 lse4[4], d4[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          lse4[q] = *reinterpret_cast<const f32x4*>(Ls + 32 * st + 8 * q + 4 * lh);
+          d4[q] = *reinterpret_cast<const f32x4*>(Ds + 32 * st + 8 * q + 4 * lh);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int rr = 32 * st + 8 * (r >> 2) + 4 * lh + (r & 3);
           const int rowi = r0 + rr;
           const bool ok = rowi < Sq && key < Sk && (!CAUSAL || key <= rowi + kv_off);
-          const float pr = ok ? fast_exp2(__builtin_fmaf(S[st][r], c, -Ls[rr])) : 0.f;
+          const float e = fast_exp2(__builtin_fmaf(S[st][r], c, -lse4[r >> 2][r & 3]));
+          const float pr = ok ? e : 0.f;
           S[st][r] = pr;
-          dP[st][r] = pr * (dP[st][r] - Ds[rr]);
+          dP[st][r] = pr * (dP[st][r] - d4[r >> 2][r & 3]);
         }
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
@@ -356,18 +384,23 @@ void bwd_dkdv_kernel(BwdParams p) {
       }
       // dV^T += dO^T P and dK^T += Q^T dS: dO^T, Q^T by transposing reads,
       // rows in the register order of P and dS
-#pragma unroll
-      for (int st = 0; st < 2; ++st)
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-        for (int dt = 0; dt < DTILES; ++dt) {
-          const int off = v_lane + (32 * st + 16 * kk) * QST + 32 * dt;
-          const u32x2 glo = lds_read_tr16(Gs + off), ghi = lds_read_tr16(Gs + off + 8 * QST);
-          dv[dt] = E::mfma(u32x4{glo[0], glo[1], ghi[0], ghi[1]}, pb[st][kk], dv[dt]);
-          const u32x2 qlo = lds_read_tr16(Qs + off), qhi = lds_read_tr16(Qs + off + 8 * QST);
-          dk[dt] = E::mfma(u32x4{qlo[0], qlo[1], qhi[0], qhi[1]}, db[st][kk], dk[dt]);
-        }
+      {
+        // MFMA j: (sub-tile st, k-step kk, column tile dt), dV (j even) or dK
+        auto load = [&](auto jc) -> u32x4 {
+          constexpr int j = decltype(jc)::value, dt = (j / 2) % DTILES;
+          constexpr int kk = (j / (2 * DTILES)) % 2, st = j / (4 * DTILES);
+          const uint16_t* src = ((j % 2) ? Qs : Gs) + v_lane + (32 * st + 16 * kk) * QST + 32 * dt;
+          const u32x2 lo = lds_read_tr16(src), hi = lds_read_tr16(src + 8 * QST);
+          return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        auto mfma = [&](auto jc, u32x4 a) {
+          constexpr int j = decltype(jc)::value, dt = (j / 2) % DTILES;
+          constexpr int kk = (j / (2 * DTILES)) % 2, st = j / (4 * DTILES);
+          if constexpr (j % 2) dk[dt] = E::mfma(a, db[st][kk], dk[dt]);
+          else dv[dt] = E::mfma(a, pb[st][kk], dv[dt]);
+        };
+        m_pipeline<8 * DTILES, kPipe>(load, mfma);
+      }
     }
   }
 

@@ -13,6 +13,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -139,5 +141,34 @@ __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_ex
 __device__ __forceinline__ int uniform(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
 constexpr float kLn2 = 0.693147180559945309417232121458f;
+
+// A run of N MFMAs as an explicit software pipeline: the LDS operand of
+// MFMA j is read LA MFMAs before it, and a scheduling fence after
+// every (MFMA j, read j + LA) pair keeps that distance from being collapsed
+// by the compiler's own scheduling.  load(j) returns MFMA j's operand,
+// mfma(j, a) issues MFMA j.
+template <int J, int N, int LA, class Load, class Mfma>
+__device__ __forceinline__ void m_pipe(Load& load, Mfma& mfma, u32x4 (&buf)[LA]) {
+  if constexpr (J < N) {
+    mfma(std::integral_constant<int, J>{}, buf[J % LA]);
+    if constexpr (J + LA < N) buf[J % LA] = load(std::integral_constant<int, J + LA>{});
+    __builtin_amdgcn_sched_barrier(0);
+    m_pipe<J + 1, N, LA>(load, mfma, buf);
+  }
+}
+template <int J, int N, int LA, class Load>
+__device__ __forceinline__ void m_prime(Load& load, u32x4 (&buf)[LA]) {
+  if constexpr (J < N && J < LA) {
+    buf[J] = load(std::integral_constant<int, J>{});
+    m_prime<J + 1, N, LA>(load, buf);
+  }
+}
+template <int N, int LA, class Load, class Mfma>
+__device__ __forceinline__ void m_pipeline(Load& load, Mfma& mfma) {
+  u32x4 buf[LA];
+  m_prime<0, N, LA>(load, buf);
+  __builtin_amdgcn_sched_barrier(0);
+  m_pipe<0, N, LA>(load, mfma, buf);
+}
 
 }  // namespace fa

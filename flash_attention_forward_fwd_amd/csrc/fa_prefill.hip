@@ -74,35 +74,6 @@ constexpr int kLookahead = FA_LOOKAHEAD;
 #endif
 constexpr int kMfmaPrio = FA_MFMA_SETPRIO;
 
-// An M step as an explicit software pipeline over its N MFMAs: the LDS
-// operand of MFMA j is read LA MFMAs before it, and a scheduling fence after
-// every (MFMA j, read j + LA) pair keeps that distance from being collapsed
-// by the compiler's own scheduling.  load(j) returns MFMA j's operand,
-// mfma(j, a) issues MFMA j.
-template <int J, int N, int LA, class Load, class Mfma>
-__device__ __forceinline__ void m_pipe(Load& load, Mfma& mfma, u32x4 (&buf)[LA]) {
-  if constexpr (J < N) {
-    mfma(std::integral_constant<int, J>{}, buf[J % LA]);
-    if constexpr (J + LA < N) buf[J % LA] = load(std::integral_constant<int, J + LA>{});
-    __builtin_amdgcn_sched_barrier(0);
-    m_pipe<J + 1, N, LA>(load, mfma, buf);
-  }
-}
-template <int J, int N, int LA, class Load>
-__device__ __forceinline__ void m_prime(Load& load, u32x4 (&buf)[LA]) {
-  if constexpr (J < N && J < LA) {
-    buf[J] = load(std::integral_constant<int, J>{});
-    m_prime<J + 1, N, LA>(load, buf);
-  }
-}
-template <int N, int LA, class Load, class Mfma>
-__device__ __forceinline__ void m_pipeline(Load& load, Mfma& mfma) {
-  u32x4 buf[LA];
-  m_prime<0, N, LA>(load, buf);
-  __builtin_amdgcn_sched_barrier(0);
-  m_pipe<0, N, LA>(load, mfma, buf);
-}
-
 // Work item -> (batch, query head, query block).  Query blocks are visited
 // heaviest first (a causal block's cost grows with its index).
 __device__ __forceinline__ void decode_item(const PrefillParams& p, int w, int& b, int& hq,
