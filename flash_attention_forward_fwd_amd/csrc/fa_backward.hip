@@ -197,22 +197,33 @@ void bwd_dq_kernel(BwdParams p) {
     }
     // lane = query row; register r of sub-tile st is key t*BN + 32 st + 8 (r/4) + 4 lh + r%4
     u32x4 db[2][2];
+    // every pair of the tile is admissible for this wave when all its rows
+    // and keys exist and (causal) the tile's last key is at or below the
+    // wave's first row's diagonal: the mask is then left out.  Every exp2 is
+    // evaluated and masked pairs are selected to 0, so the loop has no branch.
+    const bool full = rw0 + 32 <= Sq && (t + 1) * BN <= Sk && (!CAUSAL || t * BN + BN - 1 <= rw0 + kv_off);
+    auto grad = [&](auto mask_c) {
+      constexpr bool MASK = decltype(mask_c)::value;
 #pragma unroll
-    for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < 2; ++st) {
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = t * BN + 32 * st + 8 * (r >> 2) + 4 * lh + (r & 3);
-        const bool ok = row < Sq && key < Sk && (!CAUSAL || key <= row + kv_off);
-        const float pr = ok ? fast_exp2(__builtin_fmaf(S[st][r], c, -lse2)) : 0.f;
-        S[st][r] = pr * (dP[st][r] - dr);
+        for (int r = 0; r < 16; ++r) {
+          const int key = t * BN + 32 * st + 8 * (r >> 2) + 4 * lh + (r & 3);
+          const bool ok = !MASK || (row < Sq && key < Sk && (!CAUSAL || key <= row + kv_off));
+          const float e = fast_exp2(__builtin_fmaf(S[st][r], c, -lse2));
+          const float pr = ok ? e : 0.f;
+          S[st][r] = pr * (dP[st][r] - dr);
+        }
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int r0 = 8 * kk;
+          db[st][kk] = u32x4{E::pack2(S[st][r0 + 0], S[st][r0 + 1]), E::pack2(S[st][r0 + 2], S[st][r0 + 3]),
+                             E::pack2(S[st][r0 + 4], S[st][r0 + 5]), E::pack2(S[st][r0 + 6], S[st][r0 + 7])};
+        }
       }
-#pragma unroll
-      for (int kk = 0; kk < 2; ++kk) {
-        const int r0 = 8 * kk;
-        db[st][kk] = u32x4{E::pack2(S[st][r0 + 0], S[st][r0 + 1]), E::pack2(S[st][r0 + 2], S[st][r0 + 3]),
-                           E::pack2(S[st][r0 + 4], S[st][r0 + 5]), E::pack2(S[st][r0 + 6], S[st][r0 + 7])};
-      }
-    }
+    };
+    if (full) grad(std::false_type{});
+    else grad(std::true_type{});
     // dQ^T += K^T dS^T: K^T by transposing reads, keys in dS's register
     // order; MFMA j = (sub-tile st, k-step kk, column tile dt)
     {
@@ -352,36 +363,45 @@ void bwd_dkdv_kernel(BwdParams p) {
       }
       // lane = key; register r of sub-tile st is query row r0 + 32 st + 8 (r/4) + 4 lh + r%4
       u32x4 pb[2][2], db[2][2];
+      // every pair of this step is admissible for this wave when all its
+      // rows and keys exist and (causal) its last key is at or below its
+      // first row's diagonal: the mask is then left out
+      const bool full = r0 + BM <= Sq && kw0 + 32 <= Sk && (!CAUSAL || kw0 + 31 <= r0 + kv_off);
+      auto grad = [&](auto mask_c) {
+        constexpr bool MASK = decltype(mask_c)::value;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
-        // the rows' LSE and D, four consecutive rows per 16-byte read, read
-        // before any is used; every exp2 is evaluated and masked pairs are
-        // then selected to 0, so the loop has no branch
-        f32x4 lse4[4], d4[4];
+        for (int st = 0; st < 2; ++st) {
+          // the rows' LSE and D, four consecutive rows per 16-byte read, read
+          // before any is used; every exp2 is evaluated and masked pairs are
+          // then selected to 0, so the loop has no branch
+          f32x4 lse4[4], d4[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          lse4[q] = *reinterpret_cast<const f32x4*>(Ls + 32 * st + 8 * q + 4 * lh);
-          d4[q] = *reinterpret_cast<const f32x4*>(Ds + 32 * st + 8 * q + 4 * lh);
+          for (int q = 0; q < 4; ++q) {
+            lse4[q] = *reinterpret_cast<const f32x4*>(Ls + 32 * st + 8 * q + 4 * lh);
+            d4[q] = *reinterpret_cast<const f32x4*>(Ds + 32 * st + 8 * q + 4 * lh);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int rr = 32 * st + 8 * (r >> 2) + 4 * lh + (r & 3);
+            const int rowi = r0 + rr;
+            const bool ok = !MASK || (rowi < Sq && key < Sk && (!CAUSAL || key <= rowi + kv_off));
+            const float e = fast_exp2(__builtin_fmaf(S[st][r], c, -lse4[r >> 2][r & 3]));
+            const float pr = ok ? e : 0.f;
+            S[st][r] = pr;
+            dP[st][r] = pr * (dP[st][r] - d4[r >> 2][r & 3]);
+          }
+#pragma unroll
+          for (int kk = 0; kk < 2; ++kk) {
+            const int q = 8 * kk;
+            pb[st][kk] = u32x4{E::pack2(S[st][q + 0], S[st][q + 1]), E::pack2(S[st][q + 2], S[st][q + 3]),
+                               E::pack2(S[st][q + 4], S[st][q + 5]), E::pack2(S[st][q + 6], S[st][q + 7])};
+            db[st][kk] = u32x4{E::pack2(dP[st][q + 0], dP[st][q + 1]), E::pack2(dP[st][q + 2], dP[st][q + 3]),
+                               E::pack2(dP[st][q + 4], dP[st][q + 5]), E::pack2(dP[st][q + 6], dP[st][q + 7])};
+          }
         }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int rr = 32 * st + 8 * (r >> 2) + 4 * lh + (r & 3);
-          const int rowi = r0 + rr;
-          const bool ok = rowi < Sq && key < Sk && (!CAUSAL || key <= rowi + kv_off);
-          const float e = fast_exp2(__builtin_fmaf(S[st][r], c, -lse4[r >> 2][r & 3]));
-          const float pr = ok ? e : 0.f;
-          S[st][r] = pr;
-          dP[st][r] = pr * (dP[st][r] - d4[r >> 2][r & 3]);
-        }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int q = 8 * kk;
-          pb[st][kk] = u32x4{E::pack2(S[st][q + 0], S[st][q + 1]), E::pack2(S[st][q + 2], S[st][q + 3]),
-                             E::pack2(S[st][q + 4], S[st][q + 5]), E::pack2(S[st][q + 6], S[st][q + 7])};
-          db[st][kk] = u32x4{E::pack2(dP[st][q + 0], dP[st][q + 1]), E::pack2(dP[st][q + 2], dP[st][q + 3]),
-                             E::pack2(dP[st][q + 4], dP[st][q + 5]), E::pack2(dP[st][q + 6], dP[st][q + 7])};
-        }
-      }
+      };
+      if (full) grad(std::false_type{});
+      else grad(std::true_type{});
       // dV^T += dO^T P and dK^T += Q^T dS: dO^T, Q^T by transposing reads,
       // rows in the register order of P and dS
       {
