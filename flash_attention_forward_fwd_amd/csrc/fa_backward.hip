@@ -5,7 +5,8 @@
 // recomputed tile by tile, no score matrix is stored):
 //
 //   pre   D_i = sum_d dO[i,d] O[i,d]                                 (fp32)
-//   dq    per 128 query rows: S^T = K Q^T, dP^T = V dO^T,
+//   dq    per 128 query rows, 32 keys a step (few enough registers for two
+//         waves per SIMD): S^T = K Q^T, dP^T = V dO^T,
 //         P = exp2(S c - LSE_i log2 e), dS = P (dP - D_i),
 //         dQ^T += K^T dS^T                       (Q and dO stay in registers)
 //   dkdv  per 128 keys, 64 query rows a step: S = Q K^T, dP = dO V^T, P and dS as above,
@@ -31,6 +32,12 @@ constexpr int kBwdWaves = 4;        // waves per workgroup, 32 rows or keys each
 constexpr int kRowPad = 8;          // pad of tiles read by 16-byte row reads only
 constexpr int kTrPad = 32;          // pad of tiles that are also read transposed
 constexpr int kPipe = 4;            // MFMAs an LDS operand read runs ahead of its use
+// dQ kernel: keys per K/V tile, and the waves per SIMD its registers must allow
+#ifndef FA_BWD_DQ_KEYS
+#define FA_BWD_DQ_KEYS 32
+#endif
+constexpr int kDqKeys = FA_BWD_DQ_KEYS;
+constexpr int kDqWaves = kDqKeys == 32 ? 2 : 1;
 
 // A ROWS x D tile in flight between global memory and LDS: each of the
 // workgroup's threads holds N of its 16-byte chunks in registers, so the next
@@ -102,10 +109,11 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 
 // ---- dq: one workgroup per (batch, query head, 128 query rows) ------------------
 template <int D, int DT, bool CAUSAL>
-__global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 2)))
+__global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(kDqWaves, 2)))
 void bwd_dq_kernel(BwdParams p) {
   using E = Elt<DT>;
-  constexpr int BN = 64;                 // keys per tile (two 32-key sub-tiles)
+  constexpr int BN = kDqKeys;            // keys per tile (32-key sub-tiles)
+  constexpr int NST = BN / 32;
   constexpr int KSTEPS = D / 16, DTILES = D / 32;
   constexpr int KST = D + kTrPad;        // K: row reads (S) and transposed reads (dQ)
   constexpr int VST = D + kRowPad;       // V: row reads (dP)
@@ -181,7 +189,7 @@ void bwd_dq_kernel(BwdParams p) {
     if (t * BN >= wave_end) continue;
     // S^T = K Q^T and dP^T = V dO^T, the two products' MFMAs alternating,
     // each LDS operand read kPipe MFMAs ahead
-    f32x16 S[2], dP[2];
+    f32x16 S[NST], dP[NST];
     {
       auto load = [&](auto jc) -> u32x4 {
         constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
@@ -193,10 +201,10 @@ void bwd_dq_kernel(BwdParams p) {
         if constexpr (j % 2) dP[st] = E::mfma(a, gr[kk], kk == 0 ? f32x16{} : dP[st]);
         else S[st] = E::mfma(a, qr[kk], kk == 0 ? f32x16{} : S[st]);
       };
-      m_pipeline<4 * KSTEPS, kPipe>(load, mfma);
+      m_pipeline<2 * NST * KSTEPS, kPipe>(load, mfma);
     }
     // lane = query row; register r of sub-tile st is key t*BN + 32 st + 8 (r/4) + 4 lh + r%4
-    u32x4 db[2][2];
+    u32x4 db[NST][2];
     // every pair of the tile is admissible for this wave when all its rows
     // and keys exist and (causal) the tile's last key is at or below the
     // wave's first row's diagonal: the mask is then left out.  Every exp2 is
@@ -205,7 +213,7 @@ void bwd_dq_kernel(BwdParams p) {
     auto grad = [&](auto mask_c) {
       constexpr bool MASK = decltype(mask_c)::value;
 #pragma unroll
-      for (int st = 0; st < 2; ++st) {
+      for (int st = 0; st < NST; ++st) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int key = t * BN + 32 * st + 8 * (r >> 2) + 4 * lh + (r & 3);
@@ -239,7 +247,7 @@ void bwd_dq_kernel(BwdParams p) {
         constexpr int st = j / (2 * DTILES);
         dq[dt] = E::mfma(a, db[st][kk], dq[dt]);
       };
-      m_pipeline<4 * DTILES, kPipe>(load, mfma);
+      m_pipeline<2 * NST * DTILES, kPipe>(load, mfma);
     }
   }
 
