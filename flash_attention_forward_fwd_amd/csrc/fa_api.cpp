@@ -245,7 +245,11 @@ fa_status_t launch_varlen(const void* q, const void* k, const void* v, void* o, 
   p.work_items = plan.work_items;
   p.hkv_major = plan.hkv_major;
   p.persistent = plan.persistent;
-  p.xcd_map = 0;  // the varlen list is dealt by its own compacted order
+  // XCD dealing of whole kv heads (every kv head holds the same items) when
+  // the launch is persistent over one workgroup per CU
+  p.xcd_map = (plan.persistent && plan.grid == fa::kPersistentCTAs &&
+               fa::kPersistentCTAs % fa::kXcds == 0 && Hkv % fa::kXcds == 0) ? 1 : 0;
+  if (env_choice("FA_PREFILL_XCD") == 0) p.xcd_map = 0;
   fold_scale(scale, &p.c_log2, &p.q_sign);
   const hipError_t e = fa::launch_prefill(p, D, dtype, causal != 0, plan.grid,
                                           static_cast<hipStream_t>(stream));

@@ -49,7 +49,9 @@ struct PrefillParams {
   // XCD u % kXcds) and each XCD's workgroups stride over its own units'
   // items, so a kv head's K/V tiles are fetched into one L2 only.  Needs a
   // persistent grid of a multiple of kXcds workgroups and B * Hkv a multiple
-  // of kXcds; hkv_major then orders each XCD's list unit-major.
+  // of kXcds; hkv_major then orders each XCD's list unit-major.  Varlen
+  // (compacted list): whole kv heads are dealt (Hkv a multiple of kXcds),
+  // each XCD's list in block-major order.
   int xcd_map;
   float c_log2;        // |scale| * log2(e), or 1 when scale == 0
   int q_sign;          // +1, -1, or 0 (scale == 0): applied to q in registers

@@ -166,13 +166,19 @@ __device__ __forceinline__ int nth_seq_above(const uint16_t* nqb, int B, int L, 
   return 0;
 }
 
-// work item w of the compacted varlen list -> (sequence, query head, block)
+// work item w of the compacted varlen list -> (sequence, query head, block).
+// With the XCD map, w indexes XCD x's list, which holds the items of the kv
+// heads hk with hk % kXcds == x (every kv head has the same items, so the
+// XCDs' lists are alike) in the block-major order (block level descending,
+// sequence, kv head, group member): sorted by cost, which the snake rounds
+// balance best, while each kv head's K/V stays in one XCD's L2.
 __device__ __forceinline__ void varlen_item(const PrefillParams& p, const uint16_t* nqb,
-                                            int total_blocks, int w, int lane, int& b, int& hq,
-                                            int& qb) {
-  const int per = p.hkv_major ? p.gqa : p.Hq;  // items per (sequence, block)
+                                            int total_blocks, int w, int lane, bool xmap, int x,
+                                            int& b, int& hq, int& qb) {
+  // items per (sequence, block)
+  const int per = xmap ? p.Hq / kXcds : (p.hkv_major ? p.gqa : p.Hq);
   int r = w, hk = 0;
-  if (p.hkv_major) {
+  if (p.hkv_major && !xmap) {
     const int per_kv = total_blocks * p.gqa;
     hk = w / per_kv;
     r = w - hk * per_kv;
@@ -186,7 +192,12 @@ __device__ __forceinline__ void varlen_item(const PrefillParams& p, const uint16
   const int j = r / per, m = r - j * per;
   b = nth_seq_above(nqb, p.B, L, j, lane);
   qb = L;
-  hq = p.hkv_major ? hk * p.gqa + m : m;
+  if (xmap) {
+    const int ui = m / p.gqa;  // the XCD's ui-th kv head
+    hq = (ui * kXcds + x) * p.gqa + (m - ui * p.gqa);
+  } else {
+    hq = p.hkv_major ? hk * p.gqa + m : m;
+  }
 }
 
 template <int D, int DT, bool CAUSAL, bool LSE, bool VARLEN>
@@ -249,7 +260,7 @@ void prefill_kernel(PrefillParams p) {
   // The workgroups that stride over one item list: the whole grid, or with
   // the XCD map the grid's workgroups on one XCD (workgroup i runs on XCD
   // i % kXcds), which stride over the items of that XCD's units only.
-  const bool xmap = !VARLEN && p.xcd_map;
+  const bool xmap = p.xcd_map;
   const int xcd = xmap ? (int)blockIdx.x % kXcds : 0;
   const int NP = xmap ? (int)gridDim.x / kXcds : (int)gridDim.x;
   const int cta = xmap ? (int)blockIdx.x / kXcds : (int)blockIdx.x;
@@ -268,7 +279,7 @@ void prefill_kernel(PrefillParams p) {
       if (w >= work_items) break;
     }
     int b, hq, qb;
-    if (compact) varlen_item(p, nqb_tab, total_blocks, w, lane, b, hq, qb);
+    if (compact) varlen_item(p, nqb_tab, total_blocks, w, lane, xmap, xcd, b, hq, qb);
     else if (xmap) xcd_item(p, xcd, w, b, hq, qb);
     else decode_item(p, w, b, hq, qb);
     const int hk = hq / p.gqa;

@@ -65,6 +65,10 @@ CASES = [
     (list(np.random.default_rng(771).integers(0, 601, 70)), None, 8, 2, 64, True, "bf16", 0),
     # more sequences than the schedule table holds: the plain order with empty items skipped
     (list(np.random.default_rng(772).integers(0, 4, 4100)), None, 2, 1, 64, True, "bf16", 0),
+    # Hkv a multiple of 8 on a persistent launch: whole kv heads dealt to the XCDs, through
+    # the compacted list and through the plain order
+    ([300, 0, 1, 513, 256, 77, 700, 1000], None, 16, 8, 64, True, "bf16", 0),
+    (list(np.random.default_rng(773).integers(0, 4, 4100)), None, 8, 8, 64, True, "bf16", 0),
 ]
 
 
@@ -160,3 +164,16 @@ def test_varlen_empty_batch_and_empty_queries():
     cu = torch.tensor([0, 0, 0], dtype=torch.int32, device="cuda")
     cuk = torch.tensor([0, 4, 10], dtype=torch.int32, device="cuda")
     assert fa.fwd_varlen(q, k, k, cu, cuk, 0, 6, causal=True).shape == (0, 2, 64)
+
+
+def test_varlen_xcd_dealing_is_bitwise_neutral(monkeypatch):
+    # the same items with and without the XCD dealing of kv heads give identical bits
+    dtype, Hq, Hkv, D = "bf16", 16, 8, 128
+    lens = [300, 0, 1, 513, 256, 77, 700, 1000]
+    cu = offsets(lens)
+    q, k, v = packed_inputs(int(cu[-1]), int(cu[-1]), Hq, Hkv, D, dtype, 781)
+    outs = []
+    for xcd in ("off", "on"):
+        monkeypatch.setenv("FA_PREFILL_XCD", xcd)
+        outs.append(run_varlen(q, k, v, cu, cu, max(lens), max(lens), True, 1 / math.sqrt(D), dtype))
+    assert np.array_equal(outs[0], outs[1])
