@@ -38,6 +38,11 @@ constexpr int kPipe = 4;            // MFMAs an LDS operand read runs ahead of i
 #endif
 constexpr int kDqKeys = FA_BWD_DQ_KEYS;
 constexpr int kDqWaves = kDqKeys == 32 ? 2 : 1;
+// dK/dV kernel: query rows per step
+#ifndef FA_BWD_DKDV_ROWS
+#define FA_BWD_DKDV_ROWS 64
+#endif
+constexpr int kDkdvRows = FA_BWD_DKDV_ROWS;
 
 // A ROWS x D tile in flight between global memory and LDS: each of the
 // workgroup's threads holds N of its 16-byte chunks in registers, so the next
@@ -271,7 +276,8 @@ template <int D, int DT, bool CAUSAL>
 __global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void bwd_dkdv_kernel(BwdParams p) {
   using E = Elt<DT>;
-  constexpr int BM = 64;                 // query rows per step (two 32-row sub-tiles)
+  constexpr int BM = kDkdvRows;          // query rows per step (32-row sub-tiles)
+  constexpr int NST = BM / 32;
   constexpr int KSTEPS = D / 16, DTILES = D / 32;
   constexpr int QST = D + kTrPad;        // Q and dO: row reads and transposed reads
   __shared__ __attribute__((aligned(16))) uint16_t Qs[BM * QST];
@@ -355,7 +361,7 @@ void bwd_dkdv_kernel(BwdParams p) {
       // S = Q K^T and dP = dO V^T, the two products' MFMAs alternating, each
       // LDS operand read kPipe MFMAs ahead (one wave per SIMD: nothing else
       // hides the LDS latency)
-      f32x16 S[2], dP[2];
+      f32x16 S[NST], dP[NST];
       {
         auto load = [&](auto jc) -> u32x4 {
           constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
@@ -367,10 +373,10 @@ void bwd_dkdv_kernel(BwdParams p) {
           if constexpr (j % 2) dP[st] = E::mfma(a, vr[kk], kk == 0 ? f32x16{} : dP[st]);
           else S[st] = E::mfma(a, kr[kk], kk == 0 ? f32x16{} : S[st]);
         };
-        m_pipeline<4 * KSTEPS, kPipe>(load, mfma);
+        m_pipeline<2 * NST * KSTEPS, kPipe>(load, mfma);
       }
       // lane = key; register r of sub-tile st is query row r0 + 32 st + 8 (r/4) + 4 lh + r%4
-      u32x4 pb[2][2], db[2][2];
+      u32x4 pb[NST][2], db[NST][2];
       // every pair of this step is admissible for this wave when all its
       // rows and keys exist and (causal) its last key is at or below its
       // first row's diagonal: the mask is then left out
@@ -378,7 +384,7 @@ void bwd_dkdv_kernel(BwdParams p) {
       auto grad = [&](auto mask_c) {
         constexpr bool MASK = decltype(mask_c)::value;
 #pragma unroll
-        for (int st = 0; st < 2; ++st) {
+        for (int st = 0; st < NST; ++st) {
           // the rows' LSE and D, four consecutive rows per 16-byte read, read
           // before any is used; every exp2 is evaluated and masked pairs are
           // then selected to 0, so the loop has no branch
@@ -427,7 +433,7 @@ void bwd_dkdv_kernel(BwdParams p) {
           if constexpr (j % 2) dk[dt] = E::mfma(a, db[st][kk], dk[dt]);
           else dv[dt] = E::mfma(a, pb[st][kk], dv[dt]);
         };
-        m_pipeline<8 * DTILES, kPipe>(load, mfma);
+        m_pipeline<4 * NST * DTILES, kPipe>(load, mfma);
       }
     }
   }
