@@ -68,21 +68,18 @@ __device__ __forceinline__ void fetch_tile(TileRegs<D, ROWS>& t, const uint16_t*
   }
 }
 
-// Write a fetched tile to LDS rows of LST elements, applying q_sign (+1, -1,
-// 0: sign bit flipped, or zeroed).
+// Write a fetched tile to LDS rows of LST elements.
 template <int D, int ROWS, int LST>
-__device__ __forceinline__ void store_tile(uint16_t* lds, const TileRegs<D, ROWS>& t, int q_sign) {
+__device__ __forceinline__ void store_tile(uint16_t* lds, const TileRegs<D, ROWS>& t) {
   using T = TileRegs<D, ROWS>;
 #pragma unroll
   for (int i = 0; i < T::N; ++i) {
     const int c = (int)threadIdx.x + i * kBwdWaves * 64;
     const int r = c / T::CH, cc = c - r * T::CH;
-    u32x4 x = t.x[i];
-    if (q_sign < 0) x ^= 0x80008000u;
-    if (q_sign == 0) x = u32x4{0u, 0u, 0u, 0u};
-    lds_write16(lds + r * LST + cc * 8, x);
+    lds_write16(lds + r * LST + cc * 8, t.x[i]);
   }
 }
+
 
 // ---- pre: D_i = rowsum(dO * O), 8 threads per row ------------------------------
 template <int D, int DT>
@@ -183,8 +180,8 @@ void bwd_dq_kernel(BwdParams p) {
   }
   for (int t = 0; t < ntiles; ++t) {
     __syncthreads();  // the previous tile is no longer read
-    store_tile<D, BN, KST>(Ks, kt, 1);
-    store_tile<D, BN, VST>(Vs, vt, 1);
+    store_tile<D, BN, KST>(Ks, kt);
+    store_tile<D, BN, VST>(Vs, vt);
     __syncthreads();
     if (t + 1 < ntiles) {
       const int valid = min(BN, Sk - (t + 1) * BN);
@@ -298,7 +295,9 @@ void bwd_dkdv_kernel(BwdParams p) {
   const int Sq = p.Sq, Sk = p.Sk, kv_off = Sk - Sq;
   const long long kvbase = ((long long)b * p.Hkv + hk) * Sk * D;
 
-  // K and V rows as B operands: lane key li, d = 16 kk + 8 lh + e
+  // K (sign-folded: the scores come out as q_sign * S, the sign of the scale
+  // applied once here instead of to every Q tile) and V rows as B operands:
+  // lane key li, d = 16 kk + 8 lh + e
   u32x4 kr[KSTEPS], vr[KSTEPS];
 #pragma unroll
   for (int kk = 0; kk < KSTEPS; ++kk) {
@@ -307,6 +306,8 @@ void bwd_dkdv_kernel(BwdParams p) {
       x = gload16(static_cast<const uint16_t*>(p.k) + kvbase + (long long)key * D + 16 * kk + 8 * lh);
       y = gload16(static_cast<const uint16_t*>(p.v) + kvbase + (long long)key * D + 16 * kk + 8 * lh);
     }
+    if (p.q_sign < 0) x ^= 0x80008000u;
+    if (p.q_sign == 0) x = u32x4{0u, 0u, 0u, 0u};
     kr[kk] = x;
     vr[kk] = y;
   }
@@ -348,8 +349,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     {
       const int r0 = r_first + (it % nrt) * BM;
       __syncthreads();  // the previous tile is no longer read
-      store_tile<D, BM, QST>(Qs, qt, p.q_sign);
-      store_tile<D, BM, QST>(Gs, gt, 1);
+      store_tile<D, BM, QST>(Qs, qt);
+      store_tile<D, BM, QST>(Gs, gt);
       if (tid < BM) {
         Ls[tid] = lnext;
         Ds[tid] = dnext;
@@ -438,12 +439,11 @@ void bwd_dkdv_kernel(BwdParams p) {
     }
   }
 
-  // dK = scale * (dS^T Q) (Q was sign-folded: scale * q_sign restores it),
-  // dV = P^T dO: lane key li, d = 32 dt + 8 (r/4) + 4 lh + r%4
+  // dK = scale * (dS^T Q), dV = P^T dO: lane key li, d = 32 dt + 8 (r/4) + 4 lh + r%4
   if (key < Sk) {
     uint16_t* krow = static_cast<uint16_t*>(p.dk) + kvbase + (long long)key * D + 4 * lh;
     uint16_t* vrow = static_cast<uint16_t*>(p.dv) + kvbase + (long long)key * D + 4 * lh;
-    const float sc = p.scale * (float)p.q_sign;
+    const float sc = p.scale;
 #pragma unroll
     for (int dt = 0; dt < DTILES; ++dt)
 #pragma unroll
