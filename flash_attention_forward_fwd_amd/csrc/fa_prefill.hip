@@ -259,8 +259,9 @@ void prefill_kernel(PrefillParams p) {
 
   // The workgroups that stride over one item list: the whole grid, or with
   // the XCD map the grid's workgroups on one XCD (workgroup i runs on XCD
-  // i % kXcds), which stride over the items of that XCD's units only.
-  const bool xmap = p.xcd_map;
+  // i % kXcds), which stride over the items of that XCD's units only (the
+  // host sets the map only for a persistent grid of a multiple of kXcds).
+  const bool xmap = p.xcd_map && p.persistent;
   const int xcd = xmap ? (int)blockIdx.x % kXcds : 0;
   const int NP = xmap ? (int)gridDim.x / kXcds : (int)gridDim.x;
   const int cta = xmap ? (int)blockIdx.x / kXcds : (int)blockIdx.x;
