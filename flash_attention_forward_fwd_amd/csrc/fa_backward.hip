@@ -31,7 +31,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kBwdWaves = 4;        // waves per workgroup, 32 rows or keys each
 constexpr int kRowPad = 8;          // pad of tiles read by 16-byte row reads only
 constexpr int kTrPad = 32;          // pad of tiles that are also read transposed
-constexpr int kPipe = 4;            // MFMAs an LDS operand read runs ahead of its use
+// MFMAs an LDS operand read runs ahead of its use
+#ifndef FA_BWD_PIPE
+#define FA_BWD_PIPE 4
+#endif
+constexpr int kPipe = FA_BWD_PIPE;
 // dQ kernel: keys per K/V tile, and the waves per SIMD its registers must allow
 #ifndef FA_BWD_DQ_KEYS
 #define FA_BWD_DQ_KEYS 32
