@@ -45,6 +45,7 @@ HBM_PEAK_GBS = 8000.0            # MI355X HBM3E peak
 METRIC = "bf16 causal FA prefill TFLOP/s @Hq128/Hkv8/D128/Sq8192; % MFMA peak"
 PAGE_TFLOPS = 948.0              # prefill page, "Measured": persistent shipped default (MI355X)
 CALIB_BYTES = 256 << 20          # calibration copy: reads and writes 256 MiB
+PEAK_SCLK_MHZ = 2400             # shader clock the published matrix peak assumes
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "prefill_headline_traffic.json")
 DECODE_TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_l65536_traffic.json")
 KERNEL_SOURCES = ["flash_attention_forward_fwd_amd/csrc/fa_prefill.hip",
@@ -79,6 +80,83 @@ def stored_traffic(path=TRAFFIC_FILE, sources=None):
     if t.get("kernel_source_hash") != kernel_source_hash(sources):
         return None
     return t.get("hbm_bytes_per_launch")
+
+
+class ClockSampler:
+    """Samples the GPU's current shader and memory clocks (the amdgpu driver's
+    pp_dpm_sclk / pp_dpm_mclk files, the level marked '*') from a thread while
+    a timed region runs.  Dense MFMA work is power-limited, so the clock it
+    holds moves the result from box to box; this records it beside the
+    figure.  Reads files only, no GPU call."""
+
+    def __init__(self, period_s=0.002):
+        import glob
+        import threading
+        self.files = {}
+        for name in ("sclk", "mclk"):
+            found = sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{name}"))
+            if found:
+                self.files[name] = found[0]
+        self.period = period_s
+        self.samples = {name: [] for name in self.files}
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self, path):
+        try:
+            with open(path) as f:
+                for line in f:
+                    if "*" in line:
+                        m = re.search(r"(\d+)\s*Mhz", line, re.IGNORECASE)
+                        return int(m.group(1)) if m else None
+        except OSError:
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            for name, path in self.files.items():
+                v = self._read(path)
+                if v is not None:
+                    self.samples[name].append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.files:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self.files:
+            self._thread.join()
+
+    def summary(self):
+        if not any(self.samples.values()):
+            return None
+        out = {}
+        for name, v in self.samples.items():
+            if v:
+                v = sorted(v)
+                out[f"{name}_mhz"] = {"min": v[0], "median": v[len(v) // 2], "max": v[-1],
+                                      "samples": len(v)}
+        return out
+
+
+def clock_context(summary, achieved_tflops):
+    """The sampled clocks plus the matrix peak at the median shader clock held
+    during the timed region (the published peak assumes 2400 MHz) and the
+    kernel's fraction of it.  Context only: the roofline keeps the published
+    peak."""
+    if not summary or "sclk_mhz" not in summary:
+        return summary
+    mhz = summary["sclk_mhz"]["median"]
+    if mhz <= 0:
+        return summary
+    peak = MFMA_BF16_PEAK_TFLOPS * mhz / PEAK_SCLK_MHZ
+    summary["mfma_peak_at_median_sclk_tflops"] = round(peak, 1)
+    summary["frac_at_median_sclk"] = round(achieved_tflops / peak, 4)
+    return summary
 
 
 def dev(bits, dtype):
@@ -381,13 +459,14 @@ def main():
         fa.fwd(tq, tk, tv, causal=True, scale=s.scale, out=out)
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    t0 = time.perf_counter()
-    e0.record(stream)
-    for _ in range(args.steps):
-        fa.fwd(tq, tk, tv, causal=True, scale=s.scale, out=out)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with ClockSampler() as clocks:
+        t0 = time.perf_counter()
+        e0.record(stream)
+        for _ in range(args.steps):
+            fa.fwd(tq, tk, tv, causal=True, scale=s.scale, out=out)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     ms_kernel = e0.elapsed_time(e1) / args.steps
     flop = s.useful_flop()
@@ -433,6 +512,7 @@ def main():
                      "kernel": "prefill_kernel<128, bf16, causal>",
                      "avg_launch_ms": round(ms_kernel, 4),
                      "algorithmic_flop_per_launch": flop},
+        "clocks_during_prefill": clock_context(clocks.summary(), achieved),
         "parity": parity,
         "decode": dec,
         "varlen": vl,
