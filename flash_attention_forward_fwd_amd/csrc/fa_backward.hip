@@ -60,15 +60,25 @@ struct TileRegs {
 };
 
 // Load `valid` rows (row stride D elements in global memory) of a tile; rows
-// past `valid` are zero.
+// past `valid` are zero.  The tile is a buffer range that ends after its last
+// valid row, so those rows read zeros without a branch per load.  `src` and
+// `valid` are the same for every lane.
 template <int D, int ROWS>
 __device__ __forceinline__ void fetch_tile(TileRegs<D, ROWS>& t, const uint16_t* src, int valid) {
   using T = TileRegs<D, ROWS>;
+  // read from the first lane so that the range is built in scalar registers
+  const uintptr_t a = reinterpret_cast<uintptr_t>(src);
+  const uintptr_t lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a);
+  const uintptr_t hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32));
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      reinterpret_cast<uint16_t*>((hi << 32) | lo), (short)0, max(uniform(valid), 0) * D * 2,
+      kBufferFlags);
 #pragma unroll
   for (int i = 0; i < T::N; ++i) {
     const int c = (int)threadIdx.x + i * kBwdWaves * 64;
     const int r = c / T::CH, cc = c - r * T::CH;
-    t.x[i] = r < valid ? gload16(src + (long long)r * D + cc * 8) : u32x4{0u, 0u, 0u, 0u};
+    t.x[i] = __builtin_bit_cast(u32x4,
+                                __builtin_amdgcn_raw_buffer_load_b128(rs, (r * D + cc * 8) * 2, 0, 0));
   }
 }
 
