@@ -150,8 +150,8 @@ def decode_workspace_bytes(B, Hq, Hkv, D, capacity, Sq: int = 1) -> int:
 
 class DecodeWorkspace:
     """Zero-filled device workspace for decode, reusable call after call on
-    one stream (each call leaves its ticket counters at zero).  Sq > 1 sizes
-    it for multi-token decode steps of Sq query tokens."""
+    one stream (each call leaves its run-complete flags at zero).  Sq > 1
+    sizes it for multi-token decode steps of Sq query tokens."""
 
     def __init__(self, B, Hq, Hkv, D, capacity, device="cuda", Sq: int = 1):
         torch = _torch()

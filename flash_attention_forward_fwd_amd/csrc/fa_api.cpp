@@ -310,21 +310,24 @@ fa_status_t decode_impl(const void* q, const void* kc, const void* vc, const int
   p.v = vc;
   p.valid_len = valid_len;
   p.o = o;
-  size_t off_ml = 0, off_tickets = 0;
-  fa::decode_workspace_layout(B, Sq, Hq, Hkv, D, capacity, &off_ml, &off_tickets);
+  size_t off_ml = 0, off_flags = 0;
+  fa::decode_workspace_layout(B, Sq, Hq, Hkv, D, capacity, &off_ml, &off_flags);
+  const fa::DecodePlan plan = fa::decode_plan(B, Sq, Hq, Hkv, D, capacity);
   char* ws = static_cast<char*>(workspace);
   p.part_o = reinterpret_cast<float*>(ws);
   p.part_ml = reinterpret_cast<float*>(ws + off_ml);
-  p.tickets = reinterpret_cast<unsigned*>(ws + off_tickets);
+  p.flags = reinterpret_cast<unsigned*>(ws + off_flags);
   p.page_table = paged ? page_table : nullptr;
   p.page_size = page_size;
   p.pages_per_seq = pages_per_seq;
   p.num_pages = num_pages;
   p.gqa = Hq / Hkv;
   p.sq = Sq;
-  p.hpg = fa::decode_heads_per_group(p.gqa, Sq);
+  p.hpg = plan.hpg;
   p.causal = causal ? 1 : 0;
-  p.nsplit = fa::decode_num_splits(B, Hkv, capacity);
+  p.nsplit = plan.nsplit;
+  p.nmerge = plan.nmerge;
+  p.merge_cols = plan.merge_cols;
   p.B = B;
   p.Hq = Hq;
   p.Hkv = Hkv;

@@ -61,11 +61,32 @@ hipError_t launch_prefill(const PrefillParams& p, int D, int dtype, bool causal,
                           hipStream_t stream);
 
 // ---------------------------------------------------------------------------
-// Decode (Sq = 1, split-KV with an in-launch merge)
+// Decode (Sq = 1 and few-token steps; split-KV merged inside the launch)
 // ---------------------------------------------------------------------------
 constexpr int kDecodeWaves = 4;
+// split workgroups a decode launch aims for (one per CU)
+#ifndef FA_DECODE_TARGET_WGS
+#define FA_DECODE_TARGET_WGS 256
+#endif
+constexpr int kDecodeTargetWGs = FA_DECODE_TARGET_WGS;
 constexpr int kDecodeChunk = 32;       // tokens per MFMA step
 constexpr int kDecodeMaxGqa = 32;      // query heads sharing one kv head (MFMA N)
+constexpr int kMinSplitChunks = 4;     // a split run holds at least this many chunks
+constexpr int kMaxSplits = 256;        // split runs per unit at most
+constexpr int kMaxMergers = 64;        // merger workgroups per launch at most
+
+// Launch plan of a decode call: `units` (batch, kv head, head group) units of
+// `cstride` record columns (query token x head), each split into at most
+// `nsplit` runs whose records `nmerge` merger workgroups per unit combine
+// (nsplit == 1: no records, no mergers).
+struct DecodePlan {
+  long long units;
+  int hpg;       // query heads per head group
+  int cstride;   // record columns: hpg * Sq
+  int nsplit;
+  int nmerge;
+  int merge_cols;  // record columns per merger
+};
 
 struct DecodeParams {
   const void* q;
@@ -73,9 +94,9 @@ struct DecodeParams {
   const void* v;
   const int32_t* valid_len;
   void* o;
-  float* part_o;       // [B*Hkv][nsplit][gqa][D] fp32
-  float* part_ml;      // [B*Hkv][nsplit][gqa][2] fp32 (m in log2 domain, l)
-  unsigned* tickets;   // [B*Hkv]
+  float* part_o;       // [units][nsplit][cstride][D] fp32 run records
+  float* part_ml;      // [units][nsplit][cstride][2] fp32 (m in log2 domain, l)
+  unsigned* flags;     // [units][nmerge][nsplit] run-complete flags, zero between calls
   // paged cache: device int32 [B][pages_per_seq] physical page of each
   // logical page of a pool [num_pages][page_size][Hkv][D]; nullptr for the
   // contiguous [B][capacity][Hkv][D] cache.  capacity = pages_per_seq *
@@ -87,18 +108,20 @@ struct DecodeParams {
   int sq;              // query tokens per sequence (1 = plain decode), <= 32
   int hpg;             // query heads per head group: min(gqa, 32 / sq)
   int causal;          // bottom-right mask among the sq query tokens
-  int nsplit;          // splits per (b, kv head)
+  int nsplit;          // split runs per unit at most
+  int nmerge;          // merger workgroups per unit (0 when nsplit == 1)
+  int merge_cols;      // record columns each merger combines (1, 2 or 4)
   int lds_bytes;       // dynamic LDS of the launch (set by the launcher)
   float c_log2;
   int q_sign;
 };
 
-int decode_num_splits(int B, int Hkv, int capacity);
 int decode_heads_per_group(int gqa, int sq);
-// Workspace layout: part_o at offset 0, part_ml at *off_ml, tickets at
-// *off_tickets (either pointer may be null); returns the total size.
+DecodePlan decode_plan(int B, int Sq, int Hq, int Hkv, int D, int capacity);
+// Workspace layout: part_o at offset 0, part_ml at *off_ml, flags at
+// *off_flags (either pointer may be null); returns the total size.
 size_t decode_workspace_layout(int B, int Sq, int Hq, int Hkv, int D, int capacity,
-                               size_t* off_ml, size_t* off_tickets);
+                               size_t* off_ml, size_t* off_flags);
 hipError_t launch_decode(const DecodeParams& p, int D, int dtype, hipStream_t stream);
 
 // ---------------------------------------------------------------------------

@@ -22,8 +22,10 @@
  *             scalar", "contiguous token-major KV").  Cache entries at or past
  *             the valid length are never read, so NaN or garbage there cannot
  *             reach O (decode PR page, review: unused V-cache NaNs must not
- *             contaminate the output).  Split-KV partials are merged inside
- *             the same launch.
+ *             contaminate the output).  Long caches are split into runs whose
+ *             partial results are merged by merger workgroups of the same
+ *             launch (split-KV, which the decode PR page names as follow-up
+ *             work); one launch per call.
  *
  * Conventions shared by every entry point
  *  - All tensor pointers are device pointers owned by the caller, contiguous,
@@ -151,8 +153,8 @@ fa_status_t fa_fwd_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causa
 
 /*
  * fa_decode_workspace_bytes -- bytes of workspace fa_decode needs for these
- * sizes (0 on invalid sizes).  The workspace holds fp32 split partials and
- * one ticket counter per (batch, kv head).
+ * sizes (0 on invalid sizes).  The workspace holds the fp32 partial results
+ * of the split runs and one run-complete flag per (run, merger workgroup).
  */
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int capacity);
 
@@ -168,10 +170,12 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int capacity);
  *               causal mask admits every valid token, so it changes nothing.
  *   workspace : device memory of at least fa_decode_workspace_bytes(...) bytes,
  *               256-byte aligned, zero-filled by the caller once when it is
- *               allocated.  Every call leaves its ticket counters at zero again,
- *               so it can be reused call after call on one stream.  Two calls
- *               in flight at once must not share a workspace.
- * Tokens at or past the valid length are never loaded.
+ *               allocated.  Every call leaves its flags at zero again, so it
+ *               can be reused call after call on one stream.  Two calls in
+ *               flight at once must not share a workspace.
+ * Tokens at or past the valid length are never loaded.  The split plan is
+ * made on the device from the valid length: a short length is handled by one
+ * workgroup that writes O itself.  Repeated calls give identical bits.
  * One batch's cache must fit 32-bit byte offsets: capacity * Hkv * D * 2 <=
  * INT_MAX, else FA_ERR_SHAPE.
  */

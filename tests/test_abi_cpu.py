@@ -196,7 +196,7 @@ def test_decode_multi_workspace_grows_with_tokens():
     one = lib.fa_decode_workspace_bytes(1, 8, 2, 128, 65536)
     assert lib.fa_decode_multi_workspace_bytes(1, 1, 8, 2, 128, 65536) == one
     four = lib.fa_decode_multi_workspace_bytes(1, 4, 8, 2, 128, 65536)
-    assert four >= 4 * one - 4096
+    assert four >= 3 * one  # records grow with the query tokens; the flags do not
     assert lib.fa_decode_multi_workspace_bytes(1, 0, 8, 2, 128, 65536) == 0
     assert lib.fa_decode_multi_workspace_bytes(1, 33, 8, 2, 128, 65536) == 0
 

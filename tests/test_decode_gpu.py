@@ -147,7 +147,7 @@ def test_causal_equals_unmasked_and_repeat_calls_bitwise():
     q = wl.normal_bits((1, 8, 128), 33, "bf16")
     a = rig.run(q, causal=False)
     b = rig.run(q, causal=True)
-    c = rig.run(q, causal=False)  # workspace reused: tickets were reset
+    c = rig.run(q, causal=False)  # workspace reused: the run flags were lowered
     assert np.array_equal(a, b) and np.array_equal(a, c)
 
 
@@ -174,6 +174,9 @@ def test_length_zero_negative_and_clamped():
     (1, 64, 1, 64, 1024, "bf16", [777]),         # two head groups per kv head
     (2, 4, 4, 64, 700, "fp16", [1, 650]),
     (1, 8, 2, 128, 65536, "bf16", [40000]),
+    (8, 8, 2, 128, 8192, "bf16", [8192, 1, 33, 4000, 8191, 0, 6000, 129]),  # 4-column mergers
+    (4, 32, 2, 64, 4096, "fp16", [4096, 2500, 31, 3000]),  # 32 columns per unit
+    (32, 8, 2, 128, 2048, "bf16", [2048 - 7 * b for b in range(32)]),  # no split: one run per unit
 ], ids=lambda c: str(c))
 def test_decode_shapes(cfg):
     B, Hq, Hkv, D, cap, dtype, lens = cfg
@@ -189,3 +192,21 @@ def test_decode_shapes(cfg):
     out = oracle.widen(rig.run(q), dtype)
     ref = oracle_decode(rig, q, lens, 1 / np.sqrt(D))
     parity(out, ref, str(cfg))
+
+
+def test_run_flags_lowered_across_lengths():
+    """One workspace over calls whose valid lengths (and so split runs and
+    merger flags) differ from call to call; every output matches the oracle,
+    so no call sees a flag left raised by an earlier one."""
+    cap = 65536
+    rig = DecodeRig(1, 8, 2, 128, cap)
+    k = wl.normal_bits((cap, 2, 128), 81, "bf16")
+    v = wl.normal_bits((cap, 2, 128), 82, "bf16")
+    rig.write(0, 0, k, v)
+    q = wl.normal_bits((1, 8, 128), 83, "bf16")
+    for L in (65536, 3000, 65536, 100, 40000, 129, 65500):
+        print(f"\n[decode flags] L={L}", flush=True)
+        rig.set_len([L])
+        out = oracle.widen(rig.run(q), "bf16")
+        ref = oracle_decode(rig, q, [L], 1 / np.sqrt(128))
+        parity(out, ref, f"L={L}")
