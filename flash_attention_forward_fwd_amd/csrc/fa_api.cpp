@@ -310,13 +310,13 @@ fa_status_t decode_impl(const void* q, const void* kc, const void* vc, const int
   p.v = vc;
   p.valid_len = valid_len;
   p.o = o;
-  size_t off_ml = 0, off_flags = 0;
-  fa::decode_workspace_layout(B, Sq, Hq, Hkv, D, capacity, &off_ml, &off_flags);
+  size_t off_o = 0, off_ml = 0;
+  fa::decode_workspace_layout(B, Sq, Hq, Hkv, D, capacity, &off_o, &off_ml);
   const fa::DecodePlan plan = fa::decode_plan(B, Sq, Hq, Hkv, D, capacity);
   char* ws = static_cast<char*>(workspace);
-  p.part_o = reinterpret_cast<float*>(ws);
+  p.flags = reinterpret_cast<unsigned*>(ws);
+  p.part_o = reinterpret_cast<float*>(ws + off_o);
   p.part_ml = reinterpret_cast<float*>(ws + off_ml);
-  p.flags = reinterpret_cast<unsigned*>(ws + off_flags);
   p.page_table = paged ? page_table : nullptr;
   p.page_size = page_size;
   p.pages_per_seq = pages_per_seq;

@@ -50,6 +50,7 @@
 #include "fa_internal.h"
 
 namespace fa {
+
 namespace {
 
 constexpr int kSlots = 1;        // chunks in flight per wave
@@ -669,7 +670,7 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
     }
   }
   __syncthreads();
-  float* scratch = wml + NW * cstride * 2;  // merge weights and per-column sums
+  float* merge_lds = wml + NW * cstride * 2;  // merge weights and per-column sums
   const long long recs = (long long)unit * p.nsplit;
   const __amdgpu_buffer_rsrc_t ro = __builtin_amdgcn_make_buffer_rsrc(
       p.part_o + recs * cstride * D, (short)0, p.nsplit * cstride * D * 4, kBufferFlags);
@@ -682,11 +683,11 @@ __global__ __launch_bounds__(kDecodeWaves * 64) __attribute__((amdgpu_waves_per_
 
   if (nruns == 1) {
     merge_waves<D, DT, MULTI>(wo, wml, NW, gg, cstride, ro, rml, 0, og, out_base, gh, ostride,
-                              scratch);
+                              merge_lds);
     return;
   }
   merge_waves<D, DT, MULTI>(wo, wml, NW, gg, cstride, ro, rml, split, nullptr, 0, gh, ostride,
-                            scratch);
+                            merge_lds);
   // the record is complete in memory before any flag goes up
   wait_vmem();
   __syncthreads();
@@ -769,18 +770,26 @@ DecodePlan decode_plan(int B, int Sq, int Hq, int Hkv, int D, int capacity) {
 }
 
 size_t decode_workspace_layout(int B, int Sq, int Hq, int Hkv, int D, int capacity,
-                               size_t* off_ml, size_t* off_flags) {
+                               size_t* off_o, size_t* off_ml) {
+  // The flags come first, in a region of fixed size (the most any split
+  // launch raises: units x mergers <= kMaxMergers, runs <= kMaxSplits), so
+  // that whatever shapes share a workspace, the flags of every call sit
+  // where no call writes anything but flags -- and every completed call
+  // leaves them at zero.  Records follow.
   const DecodePlan pl = decode_plan(B, Sq, Hq, Hkv, D, capacity);
-  const size_t recs = (pl.nsplit > 1 ? (size_t)pl.units * pl.nsplit : 0) * (size_t)pl.cstride;
-  size_t bytes = recs * (size_t)D * 4;          // part_o
+  if (pl.nsplit <= 1) {
+    if (off_o) *off_o = 0;
+    if (off_ml) *off_ml = 0;
+    return 256;
+  }
+  const size_t recs = (size_t)pl.units * pl.nsplit * (size_t)pl.cstride;
+  size_t bytes = kDecodeFlagBytes;
+  if (off_o) *off_o = bytes;
+  bytes += recs * (size_t)D * 4;                // part_o
   bytes = (bytes + 255) & ~(size_t)255;
   if (off_ml) *off_ml = bytes;
   bytes += recs * 2 * 4;                        // part_ml
-  bytes = (bytes + 255) & ~(size_t)255;
-  if (off_flags) *off_flags = bytes;
-  bytes += (size_t)pl.units * pl.nmerge * pl.nsplit * 4;  // flags
-  bytes = (bytes + 255) & ~(size_t)255;
-  return bytes > 0 ? bytes : 256;
+  return (bytes + 255) & ~(size_t)255;
 }
 
 hipError_t launch_decode(const DecodeParams& p, int D, int dtype, hipStream_t stream) {

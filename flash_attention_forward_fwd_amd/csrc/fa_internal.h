@@ -118,10 +118,12 @@ struct DecodeParams {
 
 int decode_heads_per_group(int gqa, int sq);
 DecodePlan decode_plan(int B, int Sq, int Hq, int Hkv, int D, int capacity);
-// Workspace layout: part_o at offset 0, part_ml at *off_ml, flags at
-// *off_flags (either pointer may be null); returns the total size.
+// Workspace layout: the flags at offset 0 (kDecodeFlagBytes, split launches
+// only), part_o at *off_o, part_ml at *off_ml (either pointer may be null);
+// returns the total size.
+constexpr size_t kDecodeFlagBytes = (size_t)kMaxMergers * kMaxSplits * 4;
 size_t decode_workspace_layout(int B, int Sq, int Hq, int Hkv, int D, int capacity,
-                               size_t* off_ml, size_t* off_flags);
+                               size_t* off_o, size_t* off_ml);
 hipError_t launch_decode(const DecodeParams& p, int D, int dtype, hipStream_t stream);
 
 // ---------------------------------------------------------------------------

@@ -171,8 +171,9 @@ size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int capacity);
  *   workspace : device memory of at least fa_decode_workspace_bytes(...) bytes,
  *               256-byte aligned, zero-filled by the caller once when it is
  *               allocated.  Every call leaves its flags at zero again, so it
- *               can be reused call after call on one stream.  Two calls in
- *               flight at once must not share a workspace.
+ *               can be reused call after call on one stream, also for other
+ *               shapes whose size it covers.  Two calls in flight at once must
+ *               not share a workspace.
  * Tokens at or past the valid length are never loaded.  The split plan is
  * made on the device from the valid length: a short length is handled by one
  * workgroup that writes O itself.  Repeated calls give identical bits.

@@ -210,3 +210,32 @@ def test_run_flags_lowered_across_lengths():
         out = oracle.widen(rig.run(q), "bf16")
         ref = oracle_decode(rig, q, [L], 1 / np.sqrt(128))
         parity(out, ref, f"L={L}")
+
+
+def test_workspace_reused_across_shapes():
+    """One workspace, sized for the larger of two shapes, used by fa_decode for
+    a long single-batch cache and then for a smaller two-batch cache: the
+    second call's flags must not fall on the first call's records."""
+    import torch
+    fa = _fa()
+    lib = fa.lib()
+    shapes = [(1, 8, 2, 128, 65536, [65536], 700), (2, 8, 2, 128, 4096, [3000, 17], 720)]
+    need = max(fa.decode_workspace_bytes(B, Hq, Hkv, D, cap) for B, Hq, Hkv, D, cap, _, _ in shapes)
+    buf = torch.zeros(need + 256, dtype=torch.uint8, device="cuda")
+    ws = buf.data_ptr() + (-buf.data_ptr()) % 256
+    for B, Hq, Hkv, D, cap, lens, seed in shapes:
+        print(f"\n[decode reuse] B={B} cap={cap} lens={lens}", flush=True)
+        rig = DecodeRig(B, Hq, Hkv, D, cap)
+        for b, L in enumerate(lens):
+            rig.write(b, 0, wl.normal_bits((L, Hkv, D), seed + 2 * b, "bf16"),
+                      wl.normal_bits((L, Hkv, D), seed + 2 * b + 1, "bf16"))
+        rig.set_len(lens)
+        qb = wl.normal_bits((B, Hq, D), seed + 50, "bf16")
+        q = to_dev(qb, "bf16")
+        out = torch.empty_like(q)
+        st = lib.fa_decode(q.data_ptr(), rig.kc.data_ptr(), rig.vc.data_ptr(), rig.vl.data_ptr(),
+                           cap, out.data_ptr(), B, Hq, Hkv, D, 0, 1 / np.sqrt(D), 0, ws, need,
+                           torch.cuda.current_stream().cuda_stream)
+        assert st == 0
+        ref = oracle_decode(rig, qb, lens, 1 / np.sqrt(D))
+        parity(oracle.widen(bits_of(out), "bf16"), ref, f"reuse lens={lens}")
