@@ -15,7 +15,7 @@ import math
 
 from ._lib import (FA_BF16, FA_FP16, FaError, FwdPlan, check, lib)  # noqa: F401
 
-__all__ = ["fwd", "fwd_varlen", "bwd", "decode", "decode_paged", "fwd_plan", "decode_workspace_bytes", "DecodeWorkspace", "FaError",
+__all__ = ["fwd", "fwd_varlen", "bwd", "decode", "decode_noalloc", "decode_paged", "fwd_plan", "decode_workspace_bytes", "DecodeWorkspace", "FaError",
            "lib", "build"]
 
 
@@ -213,6 +213,35 @@ def decode(q, kcache, vcache, valid_len, causal: bool = False, scale: float | No
                                    int(bool(causal)), float(scale), _dtype_code(q), workspace.ptr,
                                    workspace.nbytes, _stream_ptr(q))
         check(st, "fa_decode_multi")
+    return out
+
+
+def decode_noalloc(q, kcache, vcache, valid_len, out, causal: bool = False,
+                   scale: float | None = None):
+    """decode() for one query token through the entry point that allocates
+    nothing (fa_decode_noalloc): its workspace is built into the library, so
+    neither the call nor this wrapper allocates; `out` [B,Hq,D] is required.
+    Calls that overlap in time on one GPU race."""
+    torch = _torch()
+    if q.dim() != 3 or kcache.dim() != 4:
+        raise ValueError("q must be [B, Hq, D] and the caches [B, capacity, Hkv, D]")
+    B, Hq, D = q.shape
+    cap, Hkv = kcache.shape[1], kcache.shape[2]
+    dev = q.device
+    if dev.type != "cuda":
+        raise ValueError("decode_noalloc needs GPU tensors")
+    _check_tensor("kcache", kcache, (B, cap, Hkv, D), q.dtype, dev)
+    _check_tensor("vcache", vcache, (B, cap, Hkv, D), q.dtype, dev)
+    _check_tensor("valid_len", valid_len, (B,), torch.int32, dev)
+    _check_tensor("out", out, (B, Hq, D), q.dtype, dev)
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    if scale is None:
+        scale = 1.0 / math.sqrt(D)
+    st = lib().fa_decode_noalloc(q.data_ptr(), kcache.data_ptr(), vcache.data_ptr(),
+                                 valid_len.data_ptr(), cap, out.data_ptr(), B, Hq, Hkv, D,
+                                 int(bool(causal)), float(scale), _dtype_code(q), _stream_ptr(q))
+    check(st, "fa_decode_noalloc")
     return out
 
 

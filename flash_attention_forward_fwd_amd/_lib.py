@@ -33,6 +33,7 @@ SIGNATURES = {
     "fa_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _I, _P, ctypes.c_size_t,
                        _P]),
+    "fa_decode_noalloc": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _I, _P]),
     "fa_decode_paged": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _P, _I, _I, _I, _I, _I, _F, _I, _P,
                              ctypes.c_size_t, _P]),
     "fa_decode_multi_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I, _I]),

@@ -265,7 +265,7 @@ fa_status_t decode_impl(const void* q, const void* kc, const void* vc, const int
                         const int32_t* page_table, int page_size, int pages_per_seq,
                         int num_pages, int capacity, void* o, int B, int Sq, int Hq, int Hkv,
                         int D, int causal, float scale, int dtype, void* workspace,
-                        size_t workspace_bytes, void* stream) {
+                        size_t workspace_bytes, void* stream, bool launch = true) {
   const bool paged = page_size > 0;
   if (B < 0 || Hq < 1 || Hkv < 1 || capacity < 1) return FA_ERR_SHAPE;
   if (Sq < 1 || Sq > kMaxDecodeSq) return FA_ERR_SHAPE;
@@ -303,6 +303,7 @@ fa_status_t decode_impl(const void* q, const void* kc, const void* vc, const int
       overlaps(o, ob, valid_len, (long long)B * 4) || overlaps(o, ob, workspace, (long long)need) ||
       overlaps(o, ob, page_table, ntable * 4))
     return FA_ERR_ALIAS;
+  if (!launch) return FA_OK;  // checks only
 
   fa::DecodeParams p;
   p.q = q;
@@ -469,6 +470,22 @@ fa_status_t fa_decode(const void* q, const void* kcache, const void* vcache,
                      D, causal, scale, dtype, workspace, workspace_bytes, stream);
 }
 
+fa_status_t fa_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                              const int32_t* valid_len, int capacity, void* o, int B, int Hq,
+                              int Hkv, int D, int causal, float scale, int dtype, void* stream) {
+  // every check first, against a stand-in address for the built-in workspace
+  // (its size is what matters here); then the one HIP call of the set-up
+  void* const stand_in = reinterpret_cast<void*>(static_cast<uintptr_t>(256));
+  fa_status_t st = decode_impl(q, kcache, vcache, valid_len, nullptr, 0, 0, 0, capacity, o, B, 1,
+                               Hq, Hkv, D, causal, scale, dtype, stand_in,
+                               fa::kDecodeScratchBytes, stream, false);
+  if (st != FA_OK || B == 0) return st;
+  void* ws = nullptr;
+  if (fa::decode_scratch(&ws) != hipSuccess) return FA_ERR_HIP;
+  return decode_impl(q, kcache, vcache, valid_len, nullptr, 0, 0, 0, capacity, o, B, 1, Hq, Hkv,
+                     D, causal, scale, dtype, ws, fa::kDecodeScratchBytes, stream);
+}
+
 fa_status_t fa_decode_multi(const void* q, const void* kcache, const void* vcache,
                             const int32_t* valid_len, int capacity, void* o, int B, int Sq,
                             int Hq, int Hkv, int D, int causal, float scale, int dtype,
@@ -520,7 +537,7 @@ const char* fa_status_string(int status) {
     case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED: head_dim must be 64 or 128, dtype bf16 or fp16";
     case FA_ERR_ALIGN: return "FA_ERR_ALIGN: a pointer is not 16-byte aligned";
     case FA_ERR_SCALE: return "FA_ERR_SCALE: scale is not finite";
-    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or too small";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE: workspace missing, misaligned or too small (fa_decode_noalloc: the sizes need more than its built-in workspace)";
     case FA_ERR_HIP: return "FA_ERR_HIP: the HIP runtime refused the launch";
     case FA_ERR_ALIAS: return "FA_ERR_ALIAS: the output overlaps an input";
     default: return "unknown fa status";

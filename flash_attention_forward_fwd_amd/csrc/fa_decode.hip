@@ -46,10 +46,24 @@
 // K and V of a chunk are copied global -> LDS by 16-byte buffer loads that
 // write LDS directly and bypass the caches' retention (nontemporal: each byte
 // is read once), two chunks in flight per wave.
+#include <mutex>
+
 #include "fa_common.h"
 #include "fa_internal.h"
 
 namespace fa {
+
+// Workspace of the decode entry point that allocates nothing: one array per
+// GPU, held until the process ends.  Zero at load (no initializer); every
+// completed call leaves its flags at zero again.  In host code its name is
+// only a stand-in for the symbol: its device address comes from
+// hipGetSymbolAddress (decode_scratch below).
+static __device__ __align__(256) unsigned char scratch[kDecodeScratchBytes];
+// every single-token plan fits: split runs x record columns x (D + 2) floats,
+// plus the flags and the layout's alignment
+static_assert(kDecodeFlagBytes + (size_t)kDecodeTargetWGs * kDecodeMaxGqa * (128 + 2) * 4 + 512 <=
+                  kDecodeScratchBytes,
+              "the largest single-token decode workspace fits the built-in array");
 
 namespace {
 
@@ -797,6 +811,27 @@ hipError_t launch_decode(const DecodeParams& p, int D, int dtype, hipStream_t st
     return dtype == kBF16 ? launch_p<128, kBF16>(p, stream) : launch_p<128, kFP16>(p, stream);
   }
   return dtype == kBF16 ? launch_p<64, kBF16>(p, stream) : launch_p<64, kFP16>(p, stream);
+}
+
+hipError_t decode_scratch(void** ptr) {
+  // the address of `scratch` on the current device, looked up once per device
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!addr[dev]) {
+    void* a = nullptr;
+    e = hipGetSymbolAddress(&a, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!a) return hipErrorInvalidSymbol;
+    addr[dev] = a;
+  }
+  *ptr = addr[dev];
+  return hipSuccess;
 }
 
 }  // namespace fa

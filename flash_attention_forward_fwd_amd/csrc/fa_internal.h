@@ -125,6 +125,10 @@ constexpr size_t kDecodeFlagBytes = (size_t)kMaxMergers * kMaxSplits * 4;
 size_t decode_workspace_layout(int B, int Sq, int Hq, int Hkv, int D, int capacity,
                                size_t* off_o, size_t* off_ml);
 hipError_t launch_decode(const DecodeParams& p, int D, int dtype, hipStream_t stream);
+// The built-in decode workspace of fa_decode_noalloc: its size, and its
+// device address on the current device (looked up once per device).
+constexpr size_t kDecodeScratchBytes = (size_t)8 << 20;
+hipError_t decode_scratch(void** ptr);
 
 // ---------------------------------------------------------------------------
 // Backward (dQ, dK, dV)

@@ -186,6 +186,26 @@ fa_status_t fa_decode(const void* q, const void* kcache, const void* vcache,
                       void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * fa_decode_noalloc -- fa_decode with no workspace argument and no allocation,
+ * for callers that cannot allocate device memory: code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc.
+ *   Arguments, layouts, semantics and errors as fa_decode.  The workspace is
+ *   a built-in device array of 8 MiB per GPU (every single-token decode
+ *   shape needs at most about 4.2 MiB), held until the process ends; sizes
+ *   that would need more are rejected with FA_ERR_WORKSPACE before any HIP
+ *   call.  The first call on a device looks up the array's device address
+ *   once (hipGetSymbolAddress); no call allocates or frees anything.
+ *   The array starts zeroed and every completed call leaves its flags at zero
+ *   again.  All calls on one GPU share the array: two calls that overlap in
+ *   time on one GPU (different streams, or different host threads) race and
+ *   give undefined results -- order them on one stream.
+ */
+fa_status_t fa_decode_noalloc(const void* q, const void* kcache, const void* vcache,
+                              const int32_t* valid_len, int capacity, void* o,
+                              int B, int Hq, int Hkv, int D, int causal, float scale, int dtype,
+                              void* stream);
+
+/*
  * fa_decode_paged -- fa_decode over a paged KV cache (the decode PR page
  * names paged KV as follow-up work beyond its identity page table).
  *   k_pages, v_pages : [num_pages, page_size, Hkv, D] pool of pages, each

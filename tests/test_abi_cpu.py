@@ -30,7 +30,7 @@ def test_library_loads_and_exports_header_functions():
     lib = fa.lib()
     names = declared_functions()
     assert set(names) == {"fa_fwd", "fa_fwd_lse", "fa_fwd_varlen", "fa_fwd_plan",
-                          "fa_decode_workspace_bytes", "fa_decode", "fa_decode_paged",
+                          "fa_decode_workspace_bytes", "fa_decode", "fa_decode_noalloc", "fa_decode_paged",
                           "fa_decode_multi_workspace_bytes", "fa_decode_multi",
                           "fa_decode_paged_multi", "fa_bwd_workspace_bytes", "fa_bwd",
                           "fa_status_string"}
@@ -137,6 +137,33 @@ def dec(**kw):
 ])
 def test_decode_rejects_bad_arguments(kw, code):
     assert dec(**kw) == code
+
+
+def dec_noalloc(**kw):
+    a = dict(q=FAKE, kc=FAKE + 0x1000000, vc=FAKE + 0x2000000, vl=FAKE + 0x3000000,
+             cap=128, o=FAKE + 0x4000000, B=1, Hq=8, Hkv=2, D=128, causal=0, scale=0.1, dtype=0,
+             stream=None)
+    a.update(kw)
+    return fa.lib().fa_decode_noalloc(a["q"], a["kc"], a["vc"], a["vl"], a["cap"], a["o"], a["B"],
+                                      a["Hq"], a["Hkv"], a["D"], a["causal"], a["scale"],
+                                      a["dtype"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(kc=None), NULL), (dict(vc=None), NULL), (dict(vl=None), NULL),
+    (dict(o=None), NULL), (dict(cap=0), SHAPE), (dict(B=-1), SHAPE), (dict(Hq=6, Hkv=4), SHAPE),
+    (dict(D=32), UNSUP), (dict(dtype=3), UNSUP), (dict(scale=float("nan")), SCALE),
+    (dict(kc=FAKE + 0x1000000 + 2), ALIGN), (dict(o=FAKE + 0x1000000), ALIAS),
+    (dict(cap=1 << 20, Hq=8, Hkv=8), SHAPE),
+])
+def test_decode_noalloc_rejects_bad_arguments_before_any_hip_call(kw, code):
+    # every check runs before the entry point's first HIP call (none can run
+    # here: no GPU), so each bad argument gets its own status
+    assert dec_noalloc(**kw) == code
+
+
+def test_decode_noalloc_empty_batch_is_ok():
+    assert dec_noalloc(B=0) == OK
 
 
 def paged(**kw):
