@@ -16,7 +16,10 @@ namespace fa {
 #endif
 constexpr int kPrefillWaves = FA_PREFILL_WAVES;  // waves per workgroup, 32 query rows each
 constexpr int kPrefillBM = 32 * kPrefillWaves;   // query rows per work item
-constexpr int kPrefillBN = 64;                   // keys per KV tile
+#ifndef FA_PREFILL_BN
+#define FA_PREFILL_BN 128
+#endif
+constexpr int kPrefillBN = FA_PREFILL_BN;        // keys per KV tile (64 or 128)
 constexpr int kNumCUs = 256;                     // MI355X compute units
 // two waves per SIMD: 8 waves per CU
 constexpr int kPrefillCTAsPerCU = 8 / kPrefillWaves;

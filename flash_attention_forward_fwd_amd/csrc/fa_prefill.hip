@@ -48,9 +48,9 @@ namespace {
 
 constexpr int kKPad = 8;   // K LDS row = D + 8 elements (16-byte skew per row)
 constexpr int kVPad = 32;  // V LDS row = D + 32 elements (64-byte skew per row)
-// 1 KiB LDS-image pieces per wave per tile copy: the K image of a 64-key tile
-// has 64 (D + 8) / 512 pieces, the V image 64 (D + 32) / 512; 4 waves share them
-constexpr int kDmaSlots = 5;
+// 1 KiB LDS-image pieces per wave per tile copy: the K image of a BN-key tile
+// has BN (D + 8) / 512 pieces, the V image BN (D + 32) / 512; 4 waves share them
+constexpr int kDmaSlots = (kPrefillBN * (128 + kVPad) / 512 + 3) / 4;
 
 // The exp2 reference max of a row moves only when the row's running max
 // exceeds it by more than kRescaleTau (log2 units), so p = exp2(s*c - m_ref)
@@ -207,7 +207,11 @@ void prefill_kernel(PrefillParams p) {
   constexpr int NT = kPrefillWaves * 64;
   constexpr int BM = kPrefillBM;
   constexpr int BN = kPrefillBN;
-  constexpr int NBUF = 3;            // LDS ring: tiles t-1, t, t+1 live while t+2 lands
+  // LDS ring depth: with 64-key tiles three slots (tile X is copied two
+  // phases before the lead group reads it), with 128-key tiles two (copied in
+  // the phase just before; three would not fit in LDS)
+  constexpr int NBUF = BN == 64 ? 3 : 2;
+  constexpr int NST = BN / 32;       // 32-key sub-tiles per tile
   constexpr int KST = D + kKPad;
   constexpr int VST = D + kVPad;
   constexpr int KTILE = BN * KST;    // elements per K buffer
@@ -215,7 +219,7 @@ void prefill_kernel(PrefillParams p) {
   constexpr int KSTEPS = D / 16;     // k-steps of the QK product
   constexpr int DTILES = D / 32;     // 32-wide column tiles of O
   constexpr int CH = D / 8;          // 16-byte chunks per K/V row
-  static_assert(BN == 64, "a tile is two 32-key sub-tiles");
+  static_assert(BN == 64 || BN == 128, "a tile is two or four 32-key sub-tiles");
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[NBUF * KTILE];
   __shared__ __attribute__((aligned(16))) uint16_t Vs[NBUF * VTILE];
@@ -378,30 +382,20 @@ void prefill_kernel(PrefillParams p) {
       }
     };
 
-    // ---- the three stages of a 32-key sub-tile ---------------------------------
-    // B1: row max of the sub-tile (log2 domain); move the reference max and
-    // rescale O and l when some row of the wave jumped above it by > tau
-    auto stage_max = [&](const f32x16& S) {
-      float mx = fmaxf(fmaxf(S[0], S[1]), S[2]);
+    // ---- the stages of a tile ---------------------------------------------------
+    // B1: row max of the tile (log2 domain; the tile is held as NST S
+    // accumulators of 32 keys); move the reference max and rescale O and l
+    // when some row of the wave jumped above it by > tau
+    auto stage_maxn = [&](const f32x16 (&S)[NST]) {
+      float mx = fmaxf(fmaxf(S[0][0], S[0][1]), S[1][0]);
 #pragma unroll
-      for (int r = 3; r < 15; r += 2) mx = fmaxf(mx, fmaxf(S[r], S[r + 1]));
-      mx = fmaxf(mx, S[15]);
-      mx = pair_max(mx) * c;
-      if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleTau)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2(m_run - ((m_new == -__builtin_inff()) ? 0.f : m_new));
-        l_run *= alpha;
+      for (int r = 2; r < 16; ++r) mx = fmaxf(fmaxf(mx, S[0][r]), S[1][r - 1]);
+      mx = fmaxf(mx, S[1][15]);
 #pragma unroll
-        for (int dt = 0; dt < DTILES; ++dt) oacc[dt] *= alpha;
-        m_run = m_new;
+      for (int st = 2; st < NST; ++st) {
+#pragma unroll
+        for (int r = 0; r < 16; r += 2) mx = fmaxf(fmaxf(mx, S[st][r]), S[st][r + 1]);
       }
-    };
-    // B1 over a 64-key tile held as two S accumulators
-    auto stage_max2 = [&](const f32x16& A, const f32x16& B) {
-      float mx = fmaxf(fmaxf(A[0], A[1]), B[0]);
-#pragma unroll
-      for (int r = 2; r < 16; ++r) mx = fmaxf(fmaxf(mx, A[r]), B[r - 1]);
-      mx = fmaxf(mx, B[15]);
       mx = pair_max(mx) * c;
       if (__builtin_amdgcn_ballot_w64(mx > m_run + kRescaleTau)) {
         const float m_new = fmaxf(m_run, mx);
@@ -436,7 +430,7 @@ void prefill_kernel(PrefillParams p) {
     //   QK (A): S^T = K Q^T for tile Kb; MFMA j = (sub-tile st, k-step kk)
     //     reads one 16-byte K row chunk
     auto m_step = [&](auto npv_c, auto nqk_c, const uint16_t* Vb, const uint16_t* Kb,
-                      const u32x4 (&P0)[2], const u32x4 (&P1)[2], f32x16& S0, f32x16& S1) {
+                      const u32x4 (&P)[NST][2], f32x16 (&S)[NST]) {
       constexpr int NPV = decltype(npv_c)::value, NQK = decltype(nqk_c)::value;
       auto load = [&](auto jc) -> u32x4 {
         constexpr int j = decltype(jc)::value;
@@ -455,11 +449,10 @@ void prefill_kernel(PrefillParams p) {
         constexpr int j = decltype(jc)::value;
         if constexpr (j < NPV) {
           constexpr int st = j / (2 * DTILES), kk = (j / DTILES) % 2, dt = j % DTILES;
-          oacc[dt] = E::mfma(a, st == 0 ? P0[kk] : P1[kk], oacc[dt]);
+          oacc[dt] = E::mfma(a, P[st][kk], oacc[dt]);
         } else {
           constexpr int q = j - NPV, st = q / KSTEPS, kk = q % KSTEPS;
-          f32x16& S = st == 0 ? S0 : S1;
-          S = E::mfma(a, qr[kk], kk == 0 ? f32x16{} : S);
+          S[st] = E::mfma(a, qr[kk], kk == 0 ? f32x16{} : S[st]);
         }
       };
       m_pipeline<NPV + NQK, kLookahead>(load, mfma);
@@ -468,7 +461,7 @@ void prefill_kernel(PrefillParams p) {
     // ---- ping-pong schedule ----------------------------------------------------
     // Each wave runs the step sequence M(0) V(0) M(1) V(1) ... M(ntiles) over
     // its 64-key tiles:
-    //   M(t): S_t = K_t Q^T, then O^T += V_{t-1}^T P_{t-1}^T   (32 MFMAs)
+    //   M(t): S_t = K_t Q^T, then O^T += V_{t-1}^T P_{t-1}^T   (BN / 2 MFMAs)
     //   V(t): mask (diagonal / tail only), online softmax of S_t -> P_t
     // The two waves that share a SIMD run the sequence one phase apart (waves
     // 0-3 lead, 4-7 follow): while one issues MFMAs the other runs its softmax
@@ -501,36 +494,42 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int u = 0; u < kDmaSlots; ++u) dma_offs[u] = dma_offset(lead ? KRC : VRC, u);
 
-    // prologue: the leading group copies K of tiles 0 and 1, the following V
+    // prologue: the leading group copies K of tiles 0 .. NBUF - 2, the
+    // following group V of the same tiles
     if (lead) {
       dma_tile(krs, Ks, 0, KNI, dma_offs);
-      if (ntiles > 1) dma_tile(krs, Ks + slot(1) * KTILE, 1, KNI, dma_offs);
+      if (NBUF > 2 && ntiles > 1) dma_tile(krs, Ks + slot(1) * KTILE, 1, KNI, dma_offs);
     } else {
       dma_tile(vrs, Vs, 0, VNI, dma_offs);
-      if (ntiles > 1) dma_tile(vrs, Vs + slot(1) * VTILE, 1, VNI, dma_offs);
+      if (NBUF > 2 && ntiles > 1) dma_tile(vrs, Vs + slot(1) * VTILE, 1, VNI, dma_offs);
     }
     wait_vmem();
     __syncthreads();
 
     auto run = [&](auto lag_c) {
       constexpr int LAG = decltype(lag_c)::value;
-      f32x16 S0 = f32x16{}, S1 = f32x16{};  // S of the tile between its M and V steps
-      u32x4 P0[2], P1[2];                   // P of the tile between its V and next M steps
+      f32x16 S[NST];   // S of the tile between its M and V steps
+      u32x4 P[NST][2];  // P of the tile between its V and next M steps
+#pragma unroll
+      for (int st = 0; st < NST; ++st) S[st] = f32x16{};
       auto needed = [&](int t) { return t >= 0 && t < ntiles && t * BN < wave_end; };
       // one phase of kind KIND (0: M step, 1: V step) for this wave; ALL: every
       // operation of the step is known to be needed and mask-free
       auto phase = [&](int g, auto kind_c, auto all_c) {
         constexpr int KIND = decltype(kind_c)::value;
         constexpr bool ALL = decltype(all_c)::value;
-        // the leading group copies K(X) in its V phase 2X-3, the following
-        // group V(X) in its V phase 2X-2 (tiles 0 and 1 come with the prologue)
-        const int Xld = LAG == 0 ? (g + 3) >> 1 : (g + 2) >> 1;
+        // the leading group copies K(X) in its V phase 2X - 2 NBUF + 3, the
+        // following group V(X) in its V phase 2X - 2 NBUF + 4 (tiles below
+        // NBUF - 1 come with the prologue): the slot it fills was last read
+        // in the phase before, and the tile lands before the barrier that
+        // precedes its first read
+        const int Xld = LAG == 0 ? (g + 2 * NBUF - 3) >> 1 : (g + 2 * NBUF - 4) >> 1;
         // in the straight-line body every V phase copies (a copy of tile
         // ntiles reads zeros past Sk into a ring slot no one reads), so the
         // copy and its completion wait carry no branch: a branch there lets
         // the compiler sink the softmax below the wait and expose the load
         // latency
-        const bool do_load = KIND == 1 && (ALL || (Xld >= 2 && Xld < ntiles));
+        const bool do_load = KIND == 1 && (ALL || (Xld >= NBUF - 1 && Xld < ntiles));
         if (do_load) {
           if (LAG == 0) dma_tile(krs, Ks + slot(Xld) * KTILE, Xld, KNI, dma_offs);
           else dma_tile(vrs, Vs + slot(Xld) * VTILE, Xld, VNI, dma_offs);
@@ -539,42 +538,43 @@ void prefill_kernel(PrefillParams p) {
         const int t = sidx >> 1;
         if constexpr (KIND == 0 && kMfmaPrio > 0) __builtin_amdgcn_s_setprio(kMfmaPrio);
         if (KIND == 0 && ALL) {
-          // M(t), steady state: 4*DTILES PV MFMAs (P_{t-1} dies) then 2*KSTEPS
+          // M(t), steady state: 2*NST*DTILES PV MFMAs (P_{t-1} dies) then NST*KSTEPS
           // QK MFMAs (S_t is born), LDS reads kLookahead MFMAs ahead
           const uint16_t* Kb = Ks + slot(t) * KTILE;
           const uint16_t* Vb = Vs + slot(t - 1) * VTILE;
-          m_step(std::integral_constant<int, 4 * DTILES>{}, std::integral_constant<int, 2 * KSTEPS>{},
-                 Vb, Kb, P0, P1, S0, S1);
+          m_step(std::integral_constant<int, NST * 2 * DTILES>{}, std::integral_constant<int, NST * KSTEPS>{},
+                 Vb, Kb, P, S);
         } else if (KIND == 0) {
           // M(t): PV of tile t-1, QK of tile t, each when needed by this wave
           if (sidx >= 0 && needed(t - 1)) {
             const uint16_t* Vb = Vs + slot(t - 1) * VTILE;
-            m_step(std::integral_constant<int, 4 * DTILES>{}, std::integral_constant<int, 0>{},
-                   Vb, Ks, P0, P1, S0, S1);
+            m_step(std::integral_constant<int, NST * 2 * DTILES>{}, std::integral_constant<int, 0>{},
+                   Vb, Ks, P, S);
           }
           if (sidx >= 0 && needed(t)) {
             const uint16_t* Kb = Ks + slot(t) * KTILE;
-            m_step(std::integral_constant<int, 0>{}, std::integral_constant<int, 2 * KSTEPS>{},
-                   Vs, Kb, P0, P1, S0, S1);
+            m_step(std::integral_constant<int, 0>{}, std::integral_constant<int, NST * KSTEPS>{},
+                   Vs, Kb, P, S);
           }
         } else if (ALL || (sidx >= 0 && needed(t))) {
           // V(t): mask and softmax of the 64 keys of tile t
           if (!ALL && t * BN + BN > free_keys) {
-            // register r of S0 (S1) holds key t*BN + 4*lh + off(r) (+32): keep
+            // register r of S[st] holds key t*BN + 32 st + 4*lh + off(r): keep
             // keys <= lim = min(row + Sk - Sq, Sk - 1) of this lane's row
             int lim = Sk - 1;
             if (CAUSAL) lim = min(lim, row + kv_off);
             lim -= t * BN + 4 * lh;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const int off = 8 * (r >> 2) + (r & 3);
-              S0[r] = off > lim ? -__builtin_inff() : S0[r];
-              S1[r] = off + 32 > lim ? -__builtin_inff() : S1[r];
-            }
+            for (int st = 0; st < NST; ++st)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) {
+                const int off = 32 * st + 8 * (r >> 2) + (r & 3);
+                S[st][r] = off > lim ? -__builtin_inff() : S[st][r];
+              }
           }
-          stage_max2(S0, S1);
-          stage_exp(S0, P0);
-          stage_exp(S1, P1);
+          stage_maxn(S);
+#pragma unroll
+          for (int st = 0; st < NST; ++st) stage_exp(S[st], P[st]);
         }
         if constexpr (KIND == 0 && kMfmaPrio > 0) __builtin_amdgcn_s_setprio(0);
         // each phase is its own scheduling region: nothing drifts across the
