@@ -54,12 +54,15 @@ def _check_tensor(name, t, shape, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, return_lse=False):
+def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, return_lse=False,
+        schedule: dict | None = None):
     """Dense attention forward: q [B,Hq,Sq,D], k/v [B,Hkv,Sk,D] -> o [B,Hq,Sq,D].
 
     Bottom-right aligned causal mask when causal=True.  scale defaults to
     1/sqrt(D).  With return_lse=True also returns the fp32 row log-sum-exp
-    [B,Hq,Sq]."""
+    [B,Hq,Sq].  `schedule` (keys persistent, hkv_major, xcd_map, each 0/1)
+    overrides the automatic launch schedule (fa_fwd_planned); the result is
+    bitwise the same."""
     torch = _torch()
     if q.dim() != 4 or k.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k, v must be 4-D [B, H, S, D]")
@@ -78,6 +81,16 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, ret
         scale = 1.0 / math.sqrt(D)
     dt = _dtype_code(q)
     stream = _stream_ptr(q)
+    if schedule is not None:
+        plan = FwdPlan()
+        for key in ("persistent", "hkv_major", "xcd_map"):
+            setattr(plan, key, int(schedule[key]))
+        lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev) if return_lse else None
+        st = lib().fa_fwd_planned(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                  lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Sq, Sk,
+                                  D, int(bool(causal)), float(scale), dt, ctypes.byref(plan), stream)
+        check(st, "fa_fwd_planned")
+        return (out, lse) if return_lse else out
     if return_lse:
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev)
         st = lib().fa_fwd_lse(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),

@@ -7,10 +7,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-# FA_LIB selects another build of the same library (A/B experiments); the
-# default is the in-tree build.
-LIB_PATH = os.environ.get("FA_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
-                                                     "libfa.so")
+# the in-tree build of the library
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 
 FA_OK = 0
 STATUS_NAMES = {
@@ -30,6 +28,7 @@ SIGNATURES = {
     "fa_fwd_varlen": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F, _I,
                            _P]),
     "fa_fwd_plan": (_I, [_I, _I, _I, _I, _I, _I, _I, _P]),
+    "fa_fwd_planned": (_I, [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P]),
     "fa_decode_workspace_bytes": (ctypes.c_size_t, [_I, _I, _I, _I, _I]),
     "fa_decode": (_I, [_P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _F, _I, _P, ctypes.c_size_t,
                        _P]),

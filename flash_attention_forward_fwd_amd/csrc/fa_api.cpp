@@ -49,15 +49,6 @@ void fold_scale(float scale, float* c, int* q_sign) {
   }
 }
 
-// Optional overrides for A/B experiments; unset means automatic.
-int env_choice(const char* name) {
-  const char* v = std::getenv(name);
-  if (!v || !*v) return -1;
-  if (!std::strcmp(v, "on") || !std::strcmp(v, "hkv") || !std::strcmp(v, "1")) return 1;
-  if (!std::strcmp(v, "off") || !std::strcmp(v, "qb") || !std::strcmp(v, "0")) return 0;
-  return -1;
-}
-
 fa_status_t plan_prefill(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
                          fa_fwd_plan_t* plan) {
   if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1) return FA_ERR_SHAPE;
@@ -74,14 +65,12 @@ fa_status_t plan_prefill(int B, int Hq, int Hkv, int Sq, int Sk, int D, int caus
   const int NP = fa::kPersistentCTAs;
   // persistent grid-stride once there are at least as many items as CTAs
   // (page "Dense flash-attention prefill": dense_persistent="auto")
-  int persistent = items >= NP ? 1 : 0;
-  const int ep = env_choice("FA_PREFILL_PERSISTENT");
-  if (ep >= 0) persistent = ep;
+  const int persistent = items >= NP ? 1 : 0;
   plan->persistent = persistent;
   plan->grid = persistent ? (int)(items < NP ? items : NP) : (int)items;
   // kv-head-major order when GQA and gqa*NQB*B >= 2*NP, else query-block-major
   const long long gqa = Hq / Hkv;
-  int hkv = (persistent && gqa > 1 && gqa * nqb * B >= 2LL * NP) ? 1 : 0;
+  const int hkv = (persistent && gqa > 1 && gqa * nqb * B >= 2LL * NP) ? 1 : 0;
   // XCD-aware dealing of the (batch, kv head) units, possible when the
   // persistent grid and the unit count both split evenly over the XCDs (every
   // XCD then holds the same multiset of items).  Chosen where the order is
@@ -90,13 +79,8 @@ fa_status_t plan_prefill(int B, int Hq, int Hkv, int Sq, int Sk, int D, int caus
   // rounds already span one or two kv heads.
   const bool xcd_ok = persistent && plan->grid == NP && NP % fa::kXcds == 0 &&
                       ((long long)B * Hkv) % fa::kXcds == 0;
-  int xcd = (xcd_ok && !hkv) ? 1 : 0;
-  const int eo = env_choice("FA_PREFILL_ORDER");
-  if (eo >= 0) hkv = eo;
-  const int ex = env_choice("FA_PREFILL_XCD");
-  if (ex >= 0) xcd = xcd_ok ? ex : 0;
   plan->hkv_major = hkv;
-  plan->xcd_map = xcd;
+  plan->xcd_map = (xcd_ok && !hkv) ? 1 : 0;
   // tiles streamed and tiles needing the mask, per query block (x Hq*B)
   long long tiles = 0, masked = 0;
   const long long off = (long long)Sk - Sq;
@@ -123,12 +107,33 @@ fa_status_t plan_prefill(int B, int Hq, int Hkv, int Sq, int Sk, int D, int caus
   return FA_OK;
 }
 
+// A caller's launch plan for these sizes: the automatic plan with the
+// schedule choices (persistent, hkv_major, xcd_map) taken from `want`.
+// Choices that do not fit the sizes are rejected.
+fa_status_t apply_plan(const fa_fwd_plan_t* want, fa_fwd_plan_t* plan, int B, int Hkv) {
+  if ((want->persistent != 0 && want->persistent != 1) ||
+      (want->hkv_major != 0 && want->hkv_major != 1) || (want->xcd_map != 0 && want->xcd_map != 1))
+    return FA_ERR_SHAPE;
+  const int NP = fa::kPersistentCTAs;
+  const int persistent = want->persistent && plan->work_items > 0 ? 1 : 0;
+  const int grid = persistent ? (plan->work_items < NP ? plan->work_items : NP) : plan->work_items;
+  if (want->xcd_map && !(persistent && grid == NP && NP % fa::kXcds == 0 &&
+                         ((long long)B * Hkv) % fa::kXcds == 0))
+    return FA_ERR_SHAPE;
+  plan->persistent = persistent;
+  plan->grid = grid;
+  plan->hkv_major = want->hkv_major;
+  plan->xcd_map = want->xcd_map;
+  return FA_OK;
+}
+
 fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                      int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale, int dtype,
-                     void* stream) {
+                     void* stream, const fa_fwd_plan_t* want = nullptr) {
   fa_fwd_plan_t plan;
-  const fa_status_t ps = plan_prefill(B, Hq, Hkv, Sq, Sk, D, causal, &plan);
+  fa_status_t ps = plan_prefill(B, Hq, Hkv, Sq, Sk, D, causal, &plan);
   if (ps != FA_OK) return ps;
+  if (want && (ps = apply_plan(want, &plan, B, Hkv)) != FA_OK) return ps;
   if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
   long long nq, nkv, nlse;
@@ -249,7 +254,6 @@ fa_status_t launch_varlen(const void* q, const void* k, const void* v, void* o, 
   // the launch is persistent over one workgroup per CU
   p.xcd_map = (plan.persistent && plan.grid == fa::kPersistentCTAs &&
                fa::kPersistentCTAs % fa::kXcds == 0 && Hkv % fa::kXcds == 0) ? 1 : 0;
-  if (env_choice("FA_PREFILL_XCD") == 0) p.xcd_map = 0;
   fold_scale(scale, &p.c_log2, &p.q_sign);
   const hipError_t e = fa::launch_prefill(p, D, dtype, causal != 0, plan.grid,
                                           static_cast<hipStream_t>(stream));
@@ -447,6 +451,13 @@ fa_status_t fa_fwd_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causa
                         fa_fwd_plan_t* plan) {
   if (!plan) return FA_ERR_NULL;
   return plan_prefill(B, Hq, Hkv, Sq, Sk, D, causal, plan);
+}
+
+fa_status_t fa_fwd_planned(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale,
+                           int dtype, const fa_fwd_plan_t* plan, void* stream) {
+  if (!plan) return FA_ERR_NULL;
+  return fwd_impl(q, k, v, o, lse, B, Hq, Hkv, Sq, Sk, D, causal, scale, dtype, stream, plan);
 }
 
 size_t fa_decode_workspace_bytes(int B, int Hq, int Hkv, int D, int capacity) {

@@ -152,6 +152,21 @@ fa_status_t fa_fwd_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causa
                         fa_fwd_plan_t* plan);
 
 /*
+ * fa_fwd_planned -- fa_fwd (and fa_fwd_lse when lse is not NULL) with the
+ * launch schedule chosen by the caller: `plan` holds the choices in its
+ * persistent, hkv_major and xcd_map fields (each 0 or 1; the other fields are
+ * ignored).  The schedule only decides which workgroup computes which work
+ * item and in what order, so every valid choice gives bitwise the same
+ * result; it exists to compare schedules.  Choices that do not fit the
+ * sizes -- a field not 0 or 1, or xcd_map without a persistent grid of one
+ * workgroup per CU (256) and B * Hkv a multiple of 8 -- give FA_ERR_SHAPE.
+ * Other arguments and errors as fa_fwd / fa_fwd_lse.
+ */
+fa_status_t fa_fwd_planned(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
+                           float scale, int dtype, const fa_fwd_plan_t* plan, void* stream);
+
+/*
  * fa_decode_workspace_bytes -- bytes of workspace fa_decode needs for these
  * sizes (0 on invalid sizes).  The workspace holds the fp32 partial results
  * of the split runs and one run-complete flag per (run, merger workgroup).

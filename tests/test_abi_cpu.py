@@ -29,7 +29,7 @@ def declared_functions():
 def test_library_loads_and_exports_header_functions():
     lib = fa.lib()
     names = declared_functions()
-    assert set(names) == {"fa_fwd", "fa_fwd_lse", "fa_fwd_varlen", "fa_fwd_plan",
+    assert set(names) == {"fa_fwd", "fa_fwd_lse", "fa_fwd_varlen", "fa_fwd_plan", "fa_fwd_planned",
                           "fa_decode_workspace_bytes", "fa_decode", "fa_decode_noalloc", "fa_decode_paged",
                           "fa_decode_multi_workspace_bytes", "fa_decode_multi",
                           "fa_decode_paged_multi", "fa_bwd_workspace_bytes", "fa_bwd",
@@ -37,6 +37,26 @@ def test_library_loads_and_exports_header_functions():
     for n in names:
         assert hasattr(lib, n), n
         assert n in _lib.SIGNATURES
+
+
+def test_fwd_planned_checks_the_schedule_before_any_hip_call():
+    lib = fa.lib()
+    plan = _lib.FwdPlan()
+    assert lib.fa_fwd_plan(1, 32, 8, 4096, 4096, 128, 1, ctypes.byref(plan)) == OK
+    args = [FAKE, FAKE + 0x1000000, FAKE + 0x2000000, FAKE + 0x3000000, None, 1, 32, 8, 4096, 4096,
+            128, 1, 0.1, 0]
+    assert lib.fa_fwd_planned(*args, None, None) == NULL
+    for field, value in (("persistent", 2), ("hkv_major", -1), ("xcd_map", 3)):
+        bad = _lib.FwdPlan()
+        ctypes.memmove(ctypes.byref(bad), ctypes.byref(plan), ctypes.sizeof(plan))
+        setattr(bad, field, value)
+        assert lib.fa_fwd_planned(*args, ctypes.byref(bad), None) == SHAPE, field
+    # the XCD dealing needs B * Hkv a multiple of 8
+    odd = _lib.FwdPlan()
+    odd.persistent, odd.hkv_major, odd.xcd_map = 1, 0, 1
+    args_odd = list(args)
+    args_odd[7] = 4  # Hkv = 4
+    assert lib.fa_fwd_planned(*args_odd, ctypes.byref(odd), None) == SHAPE
 
 
 def test_status_strings():

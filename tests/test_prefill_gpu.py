@@ -295,20 +295,31 @@ def test_guard_bands_untouched_and_unread():
     assert np.array_equal(out[G:G + q.size].reshape(q.shape), plain)
 
 
-def test_persistent_and_grid_launches_agree_bitwise(monkeypatch):
-    # the same items computed by the persistent grid-stride launch, in both
-    # orders, with and without the XCD dealing of (batch, kv head) units, and
-    # by one workgroup per item give identical bits
+def test_persistent_and_grid_launches_agree_bitwise():
+    # the same items computed by the persistent launch, in both orders, with
+    # and without the XCD dealing of (batch, kv head) units, and by one
+    # workgroup per item (in both orders) give identical bits (fa_fwd_planned)
+    fa = _fa()
     dtype = "bf16"
     B, Hq, Hkv, S = 2, 32, 4, 1024
-    assert _fa().fwd_plan(B, Hq, Hkv, S, S, 128, True)["xcd_map"] == 1
+    assert fa.fwd_plan(B, Hq, Hkv, S, S, 128, True)["xcd_map"] == 1
     q, k, v = shape_inputs(B, Hq, Hkv, S, S, 128, dtype, seed=106)
-    outs = []
-    for pers, order, xcd in (("off", "qb", "off"), ("on", "qb", "off"), ("on", "hkv", "off"),
-                             ("on", "qb", "on"), ("on", "hkv", "on")):
-        monkeypatch.setenv("FA_PREFILL_PERSISTENT", pers)
-        monkeypatch.setenv("FA_PREFILL_ORDER", order)
-        monkeypatch.setenv("FA_PREFILL_XCD", xcd)
-        outs.append(run_fwd(q, k, v, True, 0.088, dtype))
+    tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    outs = [run_fwd(q, k, v, True, 0.088, dtype)]  # the automatic plan
+    for pers, hkv, xcd in ((0, 0, 0), (0, 1, 0), (1, 0, 0), (1, 1, 0), (1, 0, 1), (1, 1, 1)):
+        sched = dict(persistent=pers, hkv_major=hkv, xcd_map=xcd)
+        outs.append(bits_of(fa.fwd(tq, tk, tv, causal=True, scale=0.088, schedule=sched)))
     for o in outs[1:]:
         assert np.array_equal(outs[0], o)
+
+
+def test_planned_rejects_schedules_that_do_not_fit():
+    import torch
+    fa = _fa()
+    q = torch.zeros((1, 8, 256, 64), dtype=torch.bfloat16, device="cuda")
+    k = torch.zeros((1, 2, 256, 64), dtype=torch.bfloat16, device="cuda")
+    # 8 items: no persistent grid of 256 workgroups, and B * Hkv = 2
+    with pytest.raises(fa.FaError):
+        fa.fwd(q, k, k, schedule=dict(persistent=1, hkv_major=0, xcd_map=1))
+    with pytest.raises(fa.FaError):
+        fa.fwd(q, k, k, schedule=dict(persistent=2, hkv_major=0, xcd_map=0))

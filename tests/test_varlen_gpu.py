@@ -164,16 +164,3 @@ def test_varlen_empty_batch_and_empty_queries():
     cu = torch.tensor([0, 0, 0], dtype=torch.int32, device="cuda")
     cuk = torch.tensor([0, 4, 10], dtype=torch.int32, device="cuda")
     assert fa.fwd_varlen(q, k, k, cu, cuk, 0, 6, causal=True).shape == (0, 2, 64)
-
-
-def test_varlen_xcd_dealing_is_bitwise_neutral(monkeypatch):
-    # the same items with and without the XCD dealing of kv heads give identical bits
-    dtype, Hq, Hkv, D = "bf16", 16, 8, 128
-    lens = [300, 0, 1, 513, 256, 77, 700, 1000]
-    cu = offsets(lens)
-    q, k, v = packed_inputs(int(cu[-1]), int(cu[-1]), Hq, Hkv, D, dtype, 781)
-    outs = []
-    for xcd in ("off", "on"):
-        monkeypatch.setenv("FA_PREFILL_XCD", xcd)
-        outs.append(run_varlen(q, k, v, cu, cu, max(lens), max(lens), True, 1 / math.sqrt(D), dtype))
-    assert np.array_equal(outs[0], outs[1])
