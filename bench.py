@@ -6,12 +6,16 @@ A step is one fa_fwd call on the causal GQA prefill workload of the gfx950
 prefill page's headline row (B=1, Hq=128, Hkv=8, Sq=Sk=8192, D=128, bf16,
 inputs N(0,1), scale 1/sqrt(128)), with Q/K/V already resident in HBM.
 `value` is useful TFLOP/s: 4*D per admissible (query, key) pair, causal
-pairs only.  The Sq=1 split-KV decode (B1/Hq8/Hkv2/D128, L = 65536,
-NaN-poisoned tail) is timed in the same run and reported as GB/s of
-algorithmic bytes in the "decode" object (with the same call through a page
-table and a 4-token causal step), and the packed varlen forward on a
-ragged batch (16 sequences of 256..8192 tokens, Hq32/Hkv8/D128, causal) in
-the "varlen" object.
+pairs only.  The Sq=1 split-KV decode (B1/Hq8/Hkv2/D128, L = 65536 valid
+tokens in a cache of 65536 + 128 whose last 128 rows hold bf16 quiet NaN)
+is timed in the same run and reported as GB/s of algorithmic bytes in the
+"decode" object (with the same call through a page table and a 4-token
+causal step), and the packed varlen forward on a ragged batch (16 sequences
+of 256..8192 tokens, Hq32/Hkv8/D128, causal) in the "varlen" object.  The
+"configs" object times every other prefill workload of the pages (the tiny
+case, MHA causal / non-causal / fp16, batched GQA at D128 and D64, the
+ragged 1000 x 3000 case, the Sq sweep) and decode latency per token at
+capacity 128 and at short lengths in a 65536-token cache.
 
 One JSON line is printed.  Besides the throughput it carries
   roofline      the prefill kernel's average launch time (HIP events on the
@@ -179,6 +183,18 @@ def worst_frac(got, ref):
     return float(np.max(np.abs(got - ref) / (1e-2 + 1e-2 * np.abs(ref)))) if got.size else 0.0
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_leg(prefill, decode, varlen, heads, backward=None):
     """The CPU oracle, as it stands, on this host.
 
@@ -189,6 +205,7 @@ def cpu_leg(prefill, decode, varlen, heads, backward=None):
     import numpy as np
 
     import oracle
+    cores = len(os.sched_getaffinity(0))
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -208,9 +225,10 @@ def cpu_leg(prefill, decode, varlen, heads, backward=None):
     parity = {"prefill_heads": heads,
               "prefill_worst_frac": worst_frac(oracle.widen(out_bits[:, :heads], s.dtype), ref)}
     flop = 4 * s.D * s.B * heads * s.admissible_pairs_per_head()
-    base = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+    base = {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
             "sample": f"{heads} of {s.Hq} query heads (B=1, Sq=Sk={s.Sq}, D={s.D}, causal), "
-                      f"{dt:.1f} s of float64 NumPy on {os.cpu_count()} visible CPUs"}
+                      f"{dt:.1f} s of float64 NumPy",
+            "blas_threads": int(threads), "cpu_model": cpu_model()}
     if decode is not None:
         qb, kb, vb, L, scale, dout = decode
         t0 = time.perf_counter()
@@ -262,15 +280,61 @@ def cpu_leg(prefill, decode, varlen, heads, backward=None):
     return base, parity
 
 
+def timed_calls(torch, calls, n, warmup):
+    """Mean time (us) per call of `calls` (zero-argument callables, used in
+    rotation), kernel-side: HIP events on the current stream around n calls."""
+    for i in range(warmup):
+        calls[i % len(calls)]()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(n):
+        calls[i % len(calls)]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) * 1e3 / n
+
+
+def decode_call(fa, torch, q, kc, vc, vl, out, ws, scale, causal=False):
+    """fa_decode / fa_decode_multi with its arguments marshalled once, so that a
+    timed loop costs one foreign call per launch."""
+    lib = fa.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    B, cap, Hkv, D = kc.shape
+    if q.dim() == 3:
+        Hq = q.shape[1]
+        fn, args = lib.fa_decode, (q.data_ptr(), kc.data_ptr(), vc.data_ptr(), vl.data_ptr(), cap,
+                                   out.data_ptr(), B, Hq, Hkv, D, int(causal), scale, 0, ws.ptr,
+                                   ws.nbytes, stream)
+    else:
+        Sq, Hq = q.shape[1], q.shape[2]
+        fn, args = lib.fa_decode_multi, (q.data_ptr(), kc.data_ptr(), vc.data_ptr(), vl.data_ptr(),
+                                         cap, out.data_ptr(), B, Sq, Hq, Hkv, D, int(causal), scale,
+                                         0, ws.ptr, ws.nbytes, stream)
+
+    def call():
+        st = fn(*args)
+        if st != 0:
+            raise RuntimeError(f"decode failed: {st}")
+    return call
+
+
 def bench_decode(fa, torch, steps, warmup):
-    """Sq=1 decode at capacity 65536, L=65536, NaN tail: GB/s of algorithmic
-    bytes, cold (rotating over more caches than the 256 MB MALL holds) and warm."""
+    """Sq=1 decode over L=65536 valid tokens of a cache with room for 128 more
+    whose unused rows hold bf16 quiet NaN: GB/s of algorithmic bytes, cold
+    (rotating over more caches than the 256 MB MALL holds) and warm."""
+    import numpy as np
+
     import workloads as wl
-    B, Hq, Hkv, D, cap = 1, 8, 2, 128, 65536
-    L = cap
+    B, Hq, Hkv, D = 1, 8, 2, 128
+    L = 65536
+    cap = L + 128
     copies = 9  # 9 x 64 MiB of K+V > 2 x the 256 MB last-level cache
-    kb = wl.normal_bits((B, cap, Hkv, D), 5001, "bf16")
-    vb = wl.normal_bits((B, cap, Hkv, D), 5002, "bf16")
+    kb = np.full((B, cap, Hkv, D), wl.BF16_QNAN, dtype=np.uint16)
+    vb = kb.copy()
+    kb[:, :L] = wl.normal_bits((B, L, Hkv, D), 5001, "bf16")
+    vb[:, :L] = wl.normal_bits((B, L, Hkv, D), 5002, "bf16")
     qb = wl.normal_bits((B, Hq, D), 5003, "bf16")
     kcs = [dev(kb, torch.bfloat16) for _ in range(copies)]
     vcs = [dev(vb, torch.bfloat16) for _ in range(copies)]
@@ -285,66 +349,106 @@ def bench_decode(fa, torch, steps, warmup):
     nbytes = 2 * L * Hkv * D * 2 + 2 * Hq * D * 2 + 4 * B
     res = {}
     stream = torch.cuda.current_stream()
+    calls = [decode_call(fa, torch, q, kcs[j], vcs[j], vl, out, ws, scale) for j in range(copies)]
     for mode in ("cold", "warm"):
-        for i in range(warmup):
-            j = i % copies if mode == "cold" else 0
-            fa.decode(q, kcs[j], vcs[j], vl, scale=scale, out=out, workspace=ws)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(steps):
-            j = i % copies if mode == "cold" else 0
-            fa.decode(q, kcs[j], vcs[j], vl, scale=scale, out=out, workspace=ws)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / steps
+        us = timed_calls(torch, calls if mode == "cold" else calls[:1], steps, warmup)
         res[mode] = {"us_per_call": us, "GB_s": nbytes / (us * 1e-6) / 1e9}
-    # the same caches read as pools of 256-token pages through a page table
+    # the same caches read as pools of 128-token pages through a page table
     # (identity mapping), cold
-    P = 256
+    P = 128
     kps = [kc.view(cap // P, P, Hkv, D) for kc in kcs]
     vps = [vc.view(cap // P, P, Hkv, D) for vc in vcs]
     table = torch.arange(cap // P, dtype=torch.int32, device="cuda").view(1, cap // P)
-    for i in range(warmup):
-        fa.decode_paged(q, kps[i % copies], vps[i % copies], table, vl, scale=scale, out=out,
-                        workspace=ws)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(steps):
-        fa.decode_paged(q, kps[i % copies], vps[i % copies], table, vl, scale=scale, out=out,
-                        workspace=ws)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+    lib = fa.lib()
+    st = torch.cuda.current_stream().cuda_stream
+
+    def paged_call(j):
+        args = (q.data_ptr(), kps[j].data_ptr(), vps[j].data_ptr(), table.data_ptr(), vl.data_ptr(),
+                P, cap // P, cap // P, out.data_ptr(), B, Hq, Hkv, D, 0, scale, 0, ws.ptr,
+                ws.nbytes, st)
+        return lambda: lib.fa_decode_paged(*args)
+    us = timed_calls(torch, [paged_call(j) for j in range(copies)], steps, warmup)
     res["paged"] = {"page_size": P, "us_per_call": us, "GB_s": nbytes / (us * 1e-6) / 1e9}
     # a multi-token step: 4 query tokens at the end of the same caches, causal
     Sq = 4
     q4 = dev(wl.normal_bits((B, Sq, Hq, D), 5004, "bf16"), torch.bfloat16)
     out4 = torch.empty_like(q4)
     ws4 = fa.DecodeWorkspace(B, Hq, Hkv, D, cap, Sq=Sq)
-    for i in range(warmup):
-        fa.decode(q4, kcs[i % copies], vcs[i % copies], vl, causal=True, scale=scale, out=out4,
-                  workspace=ws4)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(steps):
-        fa.decode(q4, kcs[i % copies], vcs[i % copies], vl, causal=True, scale=scale, out=out4,
-                  workspace=ws4)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    us = e0.elapsed_time(e1) * 1e3 / steps
+    calls4 = [decode_call(fa, torch, q4, kcs[j], vcs[j], vl, out4, ws4, scale, causal=True)
+              for j in range(copies)]
+    us = timed_calls(torch, calls4, steps, warmup)
     nb4 = 2 * L * Hkv * D * 2 + 2 * Sq * Hq * D * 2 + 4 * B
     res["multi"] = {"query_tokens": Sq, "causal": True, "us_per_call": us,
                     "GB_s": nb4 / (us * 1e-6) / 1e9}
-    return {"metric": "bf16 Sq=1 split-KV decode GB/s @B1/Hq8/Hkv2/D128/L65536, NaN tail",
+    return {"metric": "bf16 Sq=1 split-KV decode GB/s @B1/Hq8/Hkv2/D128/L65536, NaN tail "
+                      "(cache of 65536 + 128 tokens)",
             "value": res["cold"]["GB_s"], "unit": "GB/s", "frac_of_hbm_peak":
             res["cold"]["GB_s"] / HBM_PEAK_GBS, "us_per_call": res["cold"]["us_per_call"],
             "warm": res["warm"], "paged_cold": res["paged"], "multi_token_cold": res["multi"],
             "algorithmic_bytes": nbytes,
             "traffic": stored_traffic(DECODE_TRAFFIC_FILE, DECODE_SOURCES)}, \
         (qb, kb, vb, L, scale, first)
+
+
+def fwd_call(fa, torch, s):
+    """fa_fwd on seeded N(0,1) inputs of workload `s` with its arguments
+    marshalled once; returns (call, tensors to keep alive)."""
+    import workloads as wl
+    q, k, v = wl.prefill_inputs(s)
+    tdt = torch.bfloat16 if s.dtype == "bf16" else torch.float16
+    tq, tk, tv = dev(q, tdt), dev(k, tdt), dev(v, tdt)
+    out = torch.empty_like(tq)
+    lib = fa.lib()
+    args = (tq.data_ptr(), tk.data_ptr(), tv.data_ptr(), out.data_ptr(), s.B, s.Hq, s.Hkv, s.Sq,
+            s.Sk, s.D, int(s.causal), s.scale, 0 if s.dtype == "bf16" else 1,
+            torch.cuda.current_stream().cuda_stream)
+
+    def call():
+        st = lib.fa_fwd(*args)
+        if st != 0:
+            raise RuntimeError(f"fa_fwd failed: {st}")
+    return call, (tq, tk, tv, out)
+
+
+def bench_configs(fa, torch):
+    """Every other prefill workload of the pages (kernel-side time, HIP events
+    around back-to-back calls; about 0.1 s of calls each) and decode latency
+    per token over 128 successive valid lengths, at capacity 128 and inside a
+    65536-token cache."""
+    import workloads as wl
+    out = {}
+    for s in (wl.TINY, wl.MHA_CAUSAL, wl.MHA_FULL, wl.MHA_FP16, wl.GQA_D128, wl.GQA_D64,
+              wl.RAGGED_D128, wl.RAGGED_D64) + wl.SWEEP:
+        call, keep = fwd_call(fa, torch, s)
+        first = timed_calls(torch, [call], 3, 2)
+        n = int(min(2000, max(20, 1e5 / max(first, 1.0))))
+        us = timed_calls(torch, [call], n, 3)
+        flop = s.useful_flop()
+        tf = flop / (us * 1e-6) / 1e12
+        plan = fa.fwd_plan(s.B, s.Hq, s.Hkv, s.Sq, s.Sk, s.D, s.causal)
+        out[s.name] = {"ms": round(us / 1e3, 5), "tflops": round(tf, 1),
+                       "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
+                       "dtype": s.dtype, "causal": s.causal, "useful_flop": flop, "calls": n,
+                       "schedule": {key: plan[key] for key in ("work_items", "grid", "persistent",
+                                                               "hkv_major", "xcd_map")}}
+        del keep
+    B, Hq, Hkv, D = 1, 8, 2, 128
+    scale = 1 / math.sqrt(D)
+    for cap in (128, 65536):
+        kb = wl.normal_bits((B, cap, Hkv, D), 5101, "bf16")
+        vb = wl.normal_bits((B, cap, Hkv, D), 5102, "bf16")
+        kc, vc = dev(kb, torch.bfloat16), dev(vb, torch.bfloat16)
+        q = dev(wl.normal_bits((B, Hq, D), 5103, "bf16"), torch.bfloat16)
+        o = torch.empty_like(q)
+        ws = fa.DecodeWorkspace(B, Hq, Hkv, D, cap)
+        lens = [torch.tensor([L], dtype=torch.int32, device="cuda") for L in range(1, 129)]
+        calls = [decode_call(fa, torch, q, kc, vc, vl, o, ws, scale) for vl in lens]
+        us = timed_calls(torch, calls, 128 * 8, 128)
+        name = f"decode_b1_hq8_hkv2_d128_cap{cap}_len1to128"
+        out[name] = {"us_per_token": round(us, 3), "valid_lengths": "1..128, one call each",
+                     "calls": 128 * 8}
+        del kc, vc
+    return out
 
 
 def bench_varlen(fa, torch, steps, warmup):
@@ -431,6 +535,8 @@ def main():
                     help="also time the packed varlen forward (1) or not (0)")
     ap.add_argument("--backward", type=int, default=1,
                     help="also time the backward pass (1) or not (0)")
+    ap.add_argument("--configs", type=int, default=1,
+                    help="also time the other workloads of the pages (1) or not (0)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -489,6 +595,7 @@ def main():
                    if args.varlen else (None, None))
     bw, bw_data = (bench_backward(fa, torch, q, k, v, tq, tk, tv, s, 3, 1) if args.backward
                    else (None, None))
+    cfgs = bench_configs(fa, torch) if args.configs else None
     cpu = parity = None
     if args.cpu_sample_heads > 0:
         cpu, parity = cpu_leg((q, k, v, out_bits, s), dec_data, vl_data, args.cpu_sample_heads,
@@ -517,6 +624,7 @@ def main():
         "decode": dec,
         "varlen": vl,
         "backward": bw,
+        "configs": cfgs,
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
