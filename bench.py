@@ -430,7 +430,8 @@ def bench_configs(fa, torch):
                        "frac_of_mfma_peak": round(tf / MFMA_BF16_PEAK_TFLOPS, 4),
                        "dtype": s.dtype, "causal": s.causal, "useful_flop": flop, "calls": n,
                        "schedule": {key: plan[key] for key in ("work_items", "grid", "persistent",
-                                                               "hkv_major", "xcd_map")}}
+                                                               "hkv_major", "xcd_map",
+                                                               "split_tiles")}}
         del keep
     B, Hq, Hkv, D = 1, 8, 2, 128
     scale = 1 / math.sqrt(D)

@@ -7,6 +7,8 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
+#include <vector>
 
 #include "fa_internal.h"
 
@@ -49,8 +51,34 @@ void fold_scale(float scale, float* c, int* q_sign) {
   }
 }
 
+// KV tiles of query block qb of a dense work item (all tiles when not causal)
+long long block_tiles(long long qb, int Sq, int Sk, int causal) {
+  const int BM = fa::kPrefillBM, BN = fa::kPrefillBN;
+  long long kv_end = Sk;
+  if (causal) {
+    const long long qlast = qb * BM + BM < Sq ? qb * BM + BM : Sq;  // one past the last row
+    kv_end = qlast + (long long)Sk - Sq;
+    if (kv_end < 0) kv_end = 0;
+    if (kv_end > Sk) kv_end = Sk;
+  }
+  return (kv_end + BN - 1) / BN;
+}
+
+// workgroups of a key-split launch with at most T tiles per part: an item of
+// nt tiles has ceil(nt / T) parts, at least one
+long long split_parts(int B, int Hq, int Sq, int Sk, int causal, long long T) {
+  const long long nqb = ((long long)Sq + fa::kPrefillBM - 1) / fa::kPrefillBM;
+  long long n = 0;
+  for (long long qb = 0; qb < nqb; ++qb) {
+    const long long nt = block_tiles(qb, Sq, Sk, causal);
+    n += nt > T ? (nt + T - 1) / T : 1;
+  }
+  return n * Hq * B;
+}
+
+// `dense`: a dense batch (the key split applies); varlen plans pass false
 fa_status_t plan_prefill(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
-                         fa_fwd_plan_t* plan) {
+                         fa_fwd_plan_t* plan, bool dense = true) {
   if (B < 0 || Sq < 0 || Sk < 0 || Hq < 1 || Hkv < 1) return FA_ERR_SHAPE;
   if (Hq % Hkv != 0) return FA_ERR_SHAPE;
   if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
@@ -104,16 +132,51 @@ fa_status_t plan_prefill(int B, int Hq, int Hkv, int Sq, int Sk, int D, int caus
   }
   plan->kv_tiles = tiles * Hq * (long long)B;
   plan->masked_tiles = masked * Hq * (long long)B;
+  // Key split of an under-filled launch: the smallest tiles-per-part T whose
+  // parts still fit one workgroup per CU (the part count only falls as T
+  // grows, and T = the longest item's tile count gives the unsplit items,
+  // fewer than the CUs).  Taken when it cuts the longest item by at least
+  // kSplitMinTiles tiles, which pays for the merge of the parts.
+  if (dense && !persistent && items > 0) {
+    // the last query block has the most keys (all blocks alike when not causal)
+    const long long max_nt = block_tiles(nqb - 1, Sq, Sk, causal);
+    long long lo = fa::kSplitMinTiles, hi = max_nt;
+    if (lo < hi) {
+      while (lo < hi) {
+        const long long mid = lo + (hi - lo) / 2;
+        if (split_parts(B, Hq, Sq, Sk, causal, mid) <= fa::kSplitMaxParts) hi = mid;
+        else lo = mid + 1;
+      }
+      if (lo <= max_nt - fa::kSplitMinTiles) {
+        plan->split_tiles = (int)lo;
+        plan->grid = (int)split_parts(B, Hq, Sq, Sk, causal, lo);
+      }
+    }
+  }
   return FA_OK;
 }
 
 // A caller's launch plan for these sizes: the automatic plan with the
 // schedule choices (persistent, hkv_major, xcd_map) taken from `want`.
 // Choices that do not fit the sizes are rejected.
-fa_status_t apply_plan(const fa_fwd_plan_t* want, fa_fwd_plan_t* plan, int B, int Hkv) {
+fa_status_t apply_plan(const fa_fwd_plan_t* want, fa_fwd_plan_t* plan, int B, int Hq, int Hkv,
+                       int Sq, int Sk, int causal) {
   if ((want->persistent != 0 && want->persistent != 1) ||
-      (want->hkv_major != 0 && want->hkv_major != 1) || (want->xcd_map != 0 && want->xcd_map != 1))
+      (want->hkv_major != 0 && want->hkv_major != 1) || (want->xcd_map != 0 && want->xcd_map != 1) ||
+      want->split_tiles < 0)
     return FA_ERR_SHAPE;
+  if (want->split_tiles > 0) {
+    if (want->persistent || want->hkv_major || want->xcd_map) return FA_ERR_SHAPE;
+    const long long parts = split_parts(B, Hq, Sq, Sk, causal, want->split_tiles);
+    if (parts > fa::kSplitMaxParts) return FA_ERR_SHAPE;
+    plan->persistent = 0;
+    plan->grid = (int)parts;
+    plan->hkv_major = 0;
+    plan->xcd_map = 0;
+    plan->split_tiles = want->split_tiles;
+    return FA_OK;
+  }
+  plan->split_tiles = 0;
   const int NP = fa::kPersistentCTAs;
   const int persistent = want->persistent && plan->work_items > 0 ? 1 : 0;
   const int grid = persistent ? (plan->work_items < NP ? plan->work_items : NP) : plan->work_items;
@@ -127,13 +190,46 @@ fa_status_t apply_plan(const fa_fwd_plan_t* want, fa_fwd_plan_t* plan, int B, in
   return FA_OK;
 }
 
+// Key-split workspace, one per (device, stream): counters (zeroed here once;
+// every split launch leaves them at zero) and the part records.  Kept until
+// the process ends, as a stream's launches may still be in flight.
+struct SplitWorkspace {
+  int device;
+  void* stream;
+  void* ptr;
+};
+std::mutex g_split_mu;
+std::vector<SplitWorkspace> g_split_ws;
+
+hipError_t split_workspace(void* stream, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_split_mu);
+  for (const SplitWorkspace& w : g_split_ws)
+    if (w.device == dev && w.stream == stream) {
+      *out = w.ptr;
+      return hipSuccess;
+    }
+  void* ptr = nullptr;
+  if ((e = hipMalloc(&ptr, fa::kSplitWorkspaceBytes)) != hipSuccess) return e;
+  if ((e = hipMemsetAsync(ptr, 0, fa::kSplitCounterBytes, static_cast<hipStream_t>(stream))) !=
+      hipSuccess) {
+    (void)hipFree(ptr);
+    return e;
+  }
+  g_split_ws.push_back({dev, stream, ptr});
+  *out = ptr;
+  return hipSuccess;
+}
+
 fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                      int Hq, int Hkv, int Sq, int Sk, int D, int causal, float scale, int dtype,
                      void* stream, const fa_fwd_plan_t* want = nullptr) {
   fa_fwd_plan_t plan;
   fa_status_t ps = plan_prefill(B, Hq, Hkv, Sq, Sk, D, causal, &plan);
   if (ps != FA_OK) return ps;
-  if (want && (ps = apply_plan(want, &plan, B, Hkv)) != FA_OK) return ps;
+  if (want && (ps = apply_plan(want, &plan, B, Hq, Hkv, Sq, Sk, causal)) != FA_OK) return ps;
   if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
   long long nq, nkv, nlse;
@@ -179,6 +275,15 @@ fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
   p.persistent = plan.persistent;
   p.xcd_map = plan.xcd_map;
   fold_scale(scale, &p.c_log2, &p.q_sign);
+  p.split_tiles = plan.split_tiles;
+  p.split_cnt = nullptr;
+  p.split_rec = nullptr;
+  if (plan.split_tiles > 0) {
+    void* ws = nullptr;
+    if (split_workspace(stream, &ws) != hipSuccess) return FA_ERR_HIP;
+    p.split_cnt = static_cast<unsigned*>(ws);
+    p.split_rec = reinterpret_cast<float*>(static_cast<char*>(ws) + fa::kSplitCounterBytes);
+  }
   const hipError_t e = fa::launch_prefill(p, D, dtype, causal != 0, plan.grid,
                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;
@@ -191,7 +296,7 @@ fa_status_t varlen_impl(const void* q, const void* k, const void* v, void* o, fl
   if (total_q < 0 || total_k < 0) return FA_ERR_SHAPE;
   // the launch plan of a dense batch of B sequences of the maximum lengths
   fa_fwd_plan_t plan;
-  const fa_status_t ps = plan_prefill(B, Hq, Hkv, max_sq, max_sk, D, causal, &plan);
+  const fa_status_t ps = plan_prefill(B, Hq, Hkv, max_sq, max_sk, D, causal, &plan, false);
   if (ps != FA_OK) return ps;
   if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
   if (!std::isfinite(scale)) return FA_ERR_SCALE;
@@ -227,7 +332,7 @@ fa_status_t launch_varlen(const void* q, const void* k, const void* v, void* o, 
   if (st != FA_OK) return st;
   if (B == 0 || max_sq == 0 || total_q == 0) return FA_OK;
   fa_fwd_plan_t plan;
-  plan_prefill(B, Hq, Hkv, max_sq, max_sk, D, causal, &plan);
+  plan_prefill(B, Hq, Hkv, max_sq, max_sk, D, causal, &plan, false);
   fa::PrefillParams p;
   p.q = q;
   p.k = k;
@@ -255,6 +360,9 @@ fa_status_t launch_varlen(const void* q, const void* k, const void* v, void* o, 
   p.xcd_map = (plan.persistent && plan.grid == fa::kPersistentCTAs &&
                fa::kPersistentCTAs % fa::kXcds == 0 && Hkv % fa::kXcds == 0) ? 1 : 0;
   fold_scale(scale, &p.c_log2, &p.q_sign);
+  p.split_tiles = 0;
+  p.split_cnt = nullptr;
+  p.split_rec = nullptr;
   const hipError_t e = fa::launch_prefill(p, D, dtype, causal != 0, plan.grid,
                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

@@ -126,6 +126,36 @@ __device__ __forceinline__ void lds_write16(uint16_t* lds, u32x4 v) {
   *reinterpret_cast<u32x4*>(lds) = v;
 }
 
+// Accesses that other workgroups, on any XCD, read or write in the same
+// launch.  The XCDs' L2 caches are not coherent with each other; loads and
+// stores with the sc1 cache policy (what an agent-scope relaxed atomic access
+// compiles to) are, so records and counters cross workgroups without an L2
+// writeback or invalidate.  Order comes from waiting for the stores to
+// complete (wait_vmem) before a counter or flag says they are there.
+constexpr int kCoherent = 16;  // buffer cache policy sc1
+__device__ __forceinline__ f32x4 ld4_coherent(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCoherent));
+}
+__device__ __forceinline__ f32x2 ld2_coherent(__amdgpu_buffer_rsrc_t rs, int off) {
+  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kCoherent));
+}
+__device__ __forceinline__ void st4_coherent(__amdgpu_buffer_rsrc_t rs, int off, f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, kCoherent);
+}
+__device__ __forceinline__ void st2_coherent(__amdgpu_buffer_rsrc_t rs, int off, f32x2 v) {
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, off, 0, kCoherent);
+}
+__device__ __forceinline__ unsigned ld_flag(const unsigned* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_flag(unsigned* p, unsigned v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// returns the value before the add
+__device__ __forceinline__ unsigned add_flag(unsigned* p, unsigned v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 // max / sum of a value with the same value in lane l ^ 32 (v_permlane32_swap).
 __device__ __forceinline__ float pair_max(float x) {
   auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);

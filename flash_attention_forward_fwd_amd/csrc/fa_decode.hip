@@ -75,7 +75,6 @@ constexpr int kMergeBatch = 16;  // records per thread per round of loads
 constexpr int kThreads = kDecodeWaves * 64;
 constexpr int kSpinLimit = 1 << 20;
 constexpr int kNtPolicy = 2;     // buffer-load cache policy: nontemporal
-constexpr int kCoherent = 16;    // cache policy sc1 (agent-coherent)
 constexpr float kRescaleTau = 8.0f;  // lazy rescale threshold (log2 units)
 
 
@@ -106,26 +105,6 @@ __device__ __forceinline__ void lds_dma16_nt(__amdgpu_buffer_rsrc_t rs, void* ds
                                              int soff) {
   __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)dst, 16,
                                            voff, soff, 0, kNtPolicy);
-}
-
-// Coherent accesses to records and flags.
-__device__ __forceinline__ f32x4 ld4_coherent(__amdgpu_buffer_rsrc_t rs, int off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, off, 0, kCoherent));
-}
-__device__ __forceinline__ f32x2 ld2_coherent(__amdgpu_buffer_rsrc_t rs, int off) {
-  return __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, kCoherent));
-}
-__device__ __forceinline__ void st4_coherent(__amdgpu_buffer_rsrc_t rs, int off, f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), rs, off, 0, kCoherent);
-}
-__device__ __forceinline__ void st2_coherent(__amdgpu_buffer_rsrc_t rs, int off, f32x2 v) {
-  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, v), rs, off, 0, kCoherent);
-}
-__device__ __forceinline__ unsigned ld_flag(const unsigned* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void st_flag(unsigned* p, unsigned v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The operands of one chunk, read from LDS in one inline-asm block that also

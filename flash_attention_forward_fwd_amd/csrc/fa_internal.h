@@ -28,6 +28,18 @@ constexpr int kPersistentCTAs = kNumCUs * kPrefillCTAsPerCU;
 // launch is dispatched to XCD i % kXcds
 constexpr int kXcds = 8;
 
+// Key-split schedule for launches with fewer work items than CUs: each item's
+// key tiles are cut into parts of at most split_tiles tiles, one workgroup per
+// part, and the item's last part to finish merges the others' partial results.
+constexpr int kSplitMinTiles = 2;      // a part holds at least this many tiles
+constexpr int kSplitMaxParts = kNumCUs; // workgroups of a split launch at most
+// per-item counters (arrivals, records written), then the part records
+constexpr size_t kSplitCounterBytes = 4096;
+static_assert(kSplitMaxParts * 2 * sizeof(unsigned) <= kSplitCounterBytes, "counters fit");
+// fp32 record of one part: per wave and lane D/2 O values, then (m, l)
+constexpr size_t split_record_bytes(int D) { return (size_t)kPrefillWaves * 64 * (D / 2 + 2) * 4; }
+constexpr size_t kSplitWorkspaceBytes = kSplitCounterBytes + kSplitMaxParts * split_record_bytes(128);
+
 struct PrefillParams {
   const void* q;
   const void* k;
@@ -58,6 +70,12 @@ struct PrefillParams {
   int xcd_map;
   float c_log2;        // |scale| * log2(e), or 1 when scale == 0
   int q_sign;          // +1, -1, or 0 (scale == 0): applied to q in registers
+  // key split (dense, non-persistent, query-block-major): tiles per part, 0
+  // for none; the grid is then the number of parts.  split_cnt: 2 counters
+  // per work item, zero between launches; split_rec: one record per part.
+  int split_tiles;
+  unsigned* split_cnt;
+  float* split_rec;
 };
 
 hipError_t launch_prefill(const PrefillParams& p, int D, int dtype, bool causal, int grid,

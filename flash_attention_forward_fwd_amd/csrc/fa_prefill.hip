@@ -128,6 +128,154 @@ __device__ __forceinline__ void xcd_item(const PrefillParams& p, int x, int w, i
   qb = p.nqb - 1 - lvl;
 }
 
+// Key tiles of query block qb of a dense item (all of them when not causal).
+template <bool CAUSAL>
+__device__ __forceinline__ int dense_block_tiles(const PrefillParams& p, int qb) {
+  int kv_end = p.Sk;
+  if (CAUSAL) kv_end = min(max(min(p.Sq, qb * kPrefillBM + kPrefillBM) + p.Sk - p.Sq, 0), p.Sk);
+  return (kv_end + kPrefillBN - 1) / kPrefillBN;
+}
+
+// Split schedule: workgroup `bid` -> (work item w, part `part` of `nparts`,
+// key tiles [t0, t1) of the item).  Items run in the query-block-major order
+// of decode_item (block level descending, then batch and query head); an item
+// of nt tiles has ceil(nt / split_tiles) parts (at least one) of near-equal
+// tile counts, numbered consecutively.  The grid holds exactly the parts, so
+// every workgroup finds one; one past the end gets nparts = 0.
+template <bool CAUSAL>
+__device__ __forceinline__ void split_part(const PrefillParams& p, int bid, int& w, int& part,
+                                           int& nparts, int& t0, int& t1) {
+  const int per_lvl = p.Hq * p.B, T = p.split_tiles;
+  int r = bid;
+  nparts = 0;
+  for (int lvl = 0; lvl < p.nqb; ++lvl) {
+    const int nt = dense_block_tiles<CAUSAL>(p, p.nqb - 1 - lvl);
+    const int np = max(1, (nt + T - 1) / T);
+    if (r < np * per_lvl) {
+      const int i = r / np;
+      part = r - i * np;
+      nparts = np;
+      w = lvl * per_lvl + i;
+      t0 = part * nt / np;
+      t1 = (part + 1) * nt / np;
+      return;
+    }
+    r -= np * per_lvl;
+  }
+}
+
+// bounded wait of an item's last part for the other parts' records (those
+// parts have all started, so in practice the wait is a few microseconds)
+constexpr int kSplitSpinLimit = 1 << 20;
+
+// End of a split part (nparts > 1).  Each part took an arrival rank from
+// the item's first counter when it started (the atomic's round trip hides
+// behind the prologue loads).  Every part but the last to start stores its
+// fp32 record -- O^T unnormalized against its reference max m, m and the row
+// sum l (per wave and lane, in register order) -- waits until the stores are
+// complete, counts itself in the item's second counter and returns false.
+// The last part to start waits until that counter shows the other parts'
+// records (those parts started before it, so they are running and will
+// finish), zeroes both counters for the next launch, and forms the merged
+// result in its registers:
+//     M = max_s m_s,  O = sum_s 2^(m_s - M) O_s,  l = sum_s 2^(m_s - M) l_s
+// summed in part order with the same fused multiply-adds for its own part as
+// for the stored ones, so the bits do not depend on which part starts last.
+// It returns true and the caller writes O / l (and the LSE from M and l).
+template <int DTILES>
+__device__ __forceinline__ bool merge_parts(const PrefillParams& p, int w, int part, int nparts,
+                                            unsigned rank, unsigned* split_word,
+                                            f32x16 (&oacc)[DTILES], float& m_run,
+                                            float& l_tot) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  unsigned* cnt = p.split_cnt + 2 * w;
+  constexpr int OB = kPrefillWaves * DTILES * 4 * 1024;  // O bytes of a record
+  constexpr int REC = OB + kPrefillWaves * 64 * 8;       // record bytes
+  static_assert((size_t)REC == split_record_bytes(32 * DTILES), "record layout");
+  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+      p.split_rec, (short)0, (int)gridDim.x * REC, kBufferFlags);
+  const int first = (int)blockIdx.x - part;  // workgroup of part 0
+  auto o_off = [&](int s, int dt, int a) {
+    return (first + s) * REC + ((wave * DTILES + dt) * 4 + a) * 1024 + lane * 16;
+  };
+  auto ml_off = [&](int s) { return (first + s) * REC + OB + (wave * 64 + lane) * 8; };
+
+  if ((int)rank < nparts - 1) {
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a)
+        st4_coherent(rs, o_off(part, dt, a),
+                     f32x4{oacc[dt][4 * a], oacc[dt][4 * a + 1], oacc[dt][4 * a + 2],
+                           oacc[dt][4 * a + 3]});
+    st2_coherent(rs, ml_off(part), f32x2{m_run, l_tot});
+    wait_vmem();
+    __syncthreads();
+    if (tid == 0) add_flag(cnt + 1, 1u);
+    return false;
+  }
+  if (tid == 0) {
+    unsigned seen = 0;
+    for (int it = 0; it < kSplitSpinLimit && !seen; ++it) {
+      seen = ld_flag(cnt + 1) >= (unsigned)(nparts - 1);
+      if (!seen) __builtin_amdgcn_s_sleep(1);
+    }
+    split_word[1] = seen;
+    st_flag(cnt, 0u);
+    st_flag(cnt + 1, 0u);
+  }
+  __syncthreads();
+  if (!split_word[1]) {  // records missing: make the failure visible
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt) oacc[dt] = f32x16{} + nan;
+    m_run = nan;
+    l_tot = 1.f;
+    return true;
+  }
+  float M = m_run;
+  for (int s = 0; s < nparts; ++s)
+    if (s != part) M = fmaxf(M, ld2_coherent(rs, ml_off(s))[0]);
+  const float Mu = M == -__builtin_inff() ? 0.f : M;
+  f32x16 acc[DTILES];
+#pragma unroll
+  for (int dt = 0; dt < DTILES; ++dt) acc[dt] = f32x16{};
+  float l = 0.f;
+  for (int s = 0; s < nparts; ++s) {
+    f32x16 x[DTILES];
+    float ms, ls;
+    if (s == part) {
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt) x[dt] = oacc[dt];
+      ms = m_run;
+      ls = l_tot;
+    } else {
+#pragma unroll
+      for (int dt = 0; dt < DTILES; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 v = ld4_coherent(rs, o_off(s, dt, a));
+#pragma unroll
+          for (int i = 0; i < 4; ++i) x[dt][4 * a + i] = v[i];
+        }
+      const f32x2 ml = ld2_coherent(rs, ml_off(s));
+      ms = ml[0];
+      ls = ml[1];
+    }
+    const float f = fast_exp2(ms - Mu);
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[dt][r] = __builtin_fmaf(f, x[dt][r], acc[dt][r]);
+    l = __builtin_fmaf(f, ls, l);
+  }
+#pragma unroll
+  for (int dt = 0; dt < DTILES; ++dt) oacc[dt] = acc[dt];
+  m_run = Mu;
+  l_tot = l;
+  return true;
+}
+
 // Packed varlen schedule.  The work items are the non-empty (sequence, query
 // head, query block) triples, in the dense order: block level descending (a
 // causal block's cost grows with its index whatever sequence it belongs to),
@@ -200,9 +348,10 @@ __device__ __forceinline__ void varlen_item(const PrefillParams& p, const uint16
   }
 }
 
-template <int D, int DT, bool CAUSAL, bool LSE, bool VARLEN>
+template <int D, int DT, bool CAUSAL, bool LSE, bool VARLEN, bool SPLIT>
 __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams p) {
+  static_assert(!(SPLIT && VARLEN), "the key split is for the dense layout");
   using E = Elt<DT>;
   constexpr int NT = kPrefillWaves * 64;
   constexpr int BM = kPrefillBM;
@@ -270,6 +419,10 @@ void prefill_kernel(PrefillParams p) {
   const int NP = xmap ? (int)gridDim.x / kXcds : (int)gridDim.x;
   const int cta = xmap ? (int)blockIdx.x / kXcds : (int)blockIdx.x;
   const int list_items = xmap ? work_items / kXcds : work_items;
+  // split launches: this workgroup's part of its item, key tiles [t0, t1),
+  // and its arrival rank among the item's parts (through LDS)
+  int part = 0, nparts = 1, t0 = 0, t1 = 0;
+  __shared__ unsigned split_word[SPLIT ? 2 : 1];
   for (int round = 0;; ++round) {
     int w;
     if (p.persistent) {
@@ -281,6 +434,10 @@ void prefill_kernel(PrefillParams p) {
     } else {
       if (round > 0) break;
       w = blockIdx.x;
+      if constexpr (SPLIT) {
+        split_part<CAUSAL>(p, blockIdx.x, w, part, nparts, t0, t1);
+        if (nparts == 0) break;
+      }
       if (w >= work_items) break;
     }
     int b, hq, qb;
@@ -316,7 +473,7 @@ void prefill_kernel(PrefillParams p) {
       qbase = (long long)b * p.q_bstride + (long long)hq * Sq * D;
       kvbase = (long long)b * p.kv_bstride + (long long)hk * Sk * D;
     }
-    const int kv_off = Sk - Sq;  // bottom-right causal offset
+    int kv_off = Sk - Sq;  // bottom-right causal offset
 
     // keys [0, kv_end) are streamed for the item; this wave needs [0, wave_end)
     int kv_end = Sk, wave_end = Sk;
@@ -325,6 +482,18 @@ void prefill_kernel(PrefillParams p) {
       wave_end = min(max(min(Sq, rw0 + 32) + kv_off, 0), Sk);
     }
     if (rw0 >= Sq) wave_end = 0;
+    if constexpr (SPLIT) {
+      // a part streams keys [ks, ke) of the item.  Everything below works in
+      // key coordinates local to the part: K/V start at key ks, and Sk and
+      // the causal offset shrink by ks (a whole number of tiles), so the
+      // masks, the mask-free tile counts and the buffer bounds carry over.
+      const int ks = t0 * BN, ke = min(t1 * BN, kv_end);
+      kvbase += (long long)ks * KRS;
+      Sk -= ks;
+      kv_off -= ks;
+      kv_end = max(ke - ks, 0);
+      wave_end = min(max(wave_end - ks, 0), kv_end);
+    }
     const int ntiles = (kv_end + BN - 1) / BN;
     // tiles [0, free_tiles) are admissible for every row of this wave, tiles
     // [0, main_tiles) for every row of the workgroup (the mask-free body)
@@ -503,6 +672,9 @@ void prefill_kernel(PrefillParams p) {
       dma_tile(vrs, Vs, 0, VNI, dma_offs);
       if (NBUF > 2 && ntiles > 1) dma_tile(vrs, Vs + slot(1) * VTILE, 1, VNI, dma_offs);
     }
+    if constexpr (SPLIT) {
+      if (nparts > 1 && tid == 0) split_word[0] = add_flag(p.split_cnt + 2 * w, 1u);
+    }
     wait_vmem();
     __syncthreads();
 
@@ -607,7 +779,12 @@ void prefill_kernel(PrefillParams p) {
     (void)free_tiles;
 
     // ---- epilogue: O = O^T / l, rows < Sq --------------------------------------
-    const float l_tot = pair_sum(l_run);
+    float l_tot = pair_sum(l_run);
+    if constexpr (SPLIT) {
+      if (nparts > 1 &&
+          !merge_parts(p, w, part, nparts, split_word[0], split_word, oacc, m_run, l_tot))
+        continue;
+    }
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
     if (row < Sq) {
       uint16_t* orow = og + qbase + (long long)row * QRS + 4 * lh;
@@ -629,9 +806,9 @@ void prefill_kernel(PrefillParams p) {
   }
 }
 
-template <int D, int DT, bool CAUSAL, bool LSE, bool VARLEN>
+template <int D, int DT, bool CAUSAL, bool LSE, bool VARLEN, bool SPLIT>
 hipError_t launch_one(const PrefillParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<D, DT, CAUSAL, LSE, VARLEN>), dim3(grid),
+  hipLaunchKernelGGL((prefill_kernel<D, DT, CAUSAL, LSE, VARLEN, SPLIT>), dim3(grid),
                      dim3(kPrefillWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
@@ -640,10 +817,13 @@ template <int D, int DT, bool CAUSAL>
 hipError_t launch_c(const PrefillParams& p, int grid, hipStream_t stream) {
   const bool lse = p.lse != nullptr;
   if (p.cu_q != nullptr)
-    return lse ? launch_one<D, DT, CAUSAL, true, true>(p, grid, stream)
-               : launch_one<D, DT, CAUSAL, false, true>(p, grid, stream);
-  return lse ? launch_one<D, DT, CAUSAL, true, false>(p, grid, stream)
-             : launch_one<D, DT, CAUSAL, false, false>(p, grid, stream);
+    return lse ? launch_one<D, DT, CAUSAL, true, true, false>(p, grid, stream)
+               : launch_one<D, DT, CAUSAL, false, true, false>(p, grid, stream);
+  if (p.split_tiles > 0)
+    return lse ? launch_one<D, DT, CAUSAL, true, false, true>(p, grid, stream)
+               : launch_one<D, DT, CAUSAL, false, false, true>(p, grid, stream);
+  return lse ? launch_one<D, DT, CAUSAL, true, false, false>(p, grid, stream)
+             : launch_one<D, DT, CAUSAL, false, false, false>(p, grid, stream);
 }
 
 template <int D, int DT>

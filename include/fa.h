@@ -79,6 +79,13 @@ typedef enum {
  * B, Sq or Sk may be 0: B = 0 or Sq = 0 enqueues nothing; Sk = 0 writes O = 0.
  * One (batch, kv head) of K or V must fit 32-bit byte offsets:
  * Sk * D * 2 <= INT_MAX, else FA_ERR_SHAPE.
+ * When the shape has fewer work items than the GPU has CUs, the keys of each
+ * item are split over several workgroups (fa_fwd_plan reports split_tiles);
+ * their partial results meet in a workspace that the library allocates once
+ * per (device, stream) on the first such call, 34.6 MB held until the process
+ * ends, so that first call is not capturable in a HIP graph.  Calls on one
+ * stream reuse it in order; a graph captured with a split launch keeps using
+ * the workspace of the stream it was captured on.
  */
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o,
                    int B, int Hq, int Hkv, int Sq, int Sk, int D,
@@ -146,6 +153,12 @@ typedef struct {
                            head's K/V is fetched into one XCD's L2 only; chosen
                            for query-block-major persistent launches whose unit
                            count B * Hkv is a multiple of 8 */
+  int split_tiles;      /* 0, or: the key tiles of each work item are cut into
+                           ceil(tiles / split_tiles) parts of near-equal size,
+                           one workgroup each (grid = number of parts), merged
+                           in the launch; chosen for non-persistent launches
+                           whose longest item can be cut to at most
+                           tiles - 2 tiles per part within one workgroup per CU */
 } fa_fwd_plan_t;
 
 fa_status_t fa_fwd_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
@@ -154,13 +167,17 @@ fa_status_t fa_fwd_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causa
 /*
  * fa_fwd_planned -- fa_fwd (and fa_fwd_lse when lse is not NULL) with the
  * launch schedule chosen by the caller: `plan` holds the choices in its
- * persistent, hkv_major and xcd_map fields (each 0 or 1; the other fields are
- * ignored).  The schedule only decides which workgroup computes which work
- * item and in what order, so every valid choice gives bitwise the same
- * result; it exists to compare schedules.  Choices that do not fit the
- * sizes -- a field not 0 or 1, or xcd_map without a persistent grid of one
- * workgroup per CU (256) and B * Hkv a multiple of 8 -- give FA_ERR_SHAPE.
- * Other arguments and errors as fa_fwd / fa_fwd_lse.
+ * persistent, hkv_major, xcd_map (each 0 or 1) and split_tiles (>= 0) fields;
+ * the other fields are ignored.  Without a split the schedule only decides
+ * which workgroup computes which work item and in what order, so every such
+ * choice gives bitwise the same result.  A split (split_tiles > 0) sums each
+ * item in parts and merges them: the result then differs from the unsplit one
+ * by rounding only, and is the same bits call after call for one split_tiles.
+ * It exists to compare schedules.  Choices that do not fit the sizes -- a
+ * field out of range, xcd_map without a persistent grid of one workgroup per
+ * CU (256) and B * Hkv a multiple of 8, a split together with persistent,
+ * hkv_major or xcd_map, or a split of more than 256 parts -- give
+ * FA_ERR_SHAPE.  Other arguments and errors as fa_fwd / fa_fwd_lse.
  */
 fa_status_t fa_fwd_planned(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,

@@ -51,6 +51,15 @@ def test_fwd_planned_checks_the_schedule_before_any_hip_call():
         ctypes.memmove(ctypes.byref(bad), ctypes.byref(plan), ctypes.sizeof(plan))
         setattr(bad, field, value)
         assert lib.fa_fwd_planned(*args, ctypes.byref(bad), None) == SHAPE, field
+    # a key split: never with a persistent grid or another order, not
+    # negative, and at most 256 parts (4096 keys / 128 per tile / 1 per part
+    # x 16 blocks x 32 heads is far more)
+    for fields in (dict(split_tiles=-1), dict(split_tiles=4, persistent=1),
+                   dict(split_tiles=4, hkv_major=1), dict(split_tiles=1)):
+        bad = _lib.FwdPlan()
+        for key, value in fields.items():
+            setattr(bad, key, value)
+        assert lib.fa_fwd_planned(*args, ctypes.byref(bad), None) == SHAPE, fields
     # the XCD dealing needs B * Hkv a multiple of 8
     odd = _lib.FwdPlan()
     odd.persistent, odd.hkv_major, odd.xcd_map = 1, 0, 1
@@ -320,7 +329,55 @@ def test_work_items_and_orders():
     for c in FACTS["persistent_auto"]["cases"]:
         p = fa.fwd_plan(c["B"], c["Hq"], c["Hq"], c["Sq"], c["Sq"], 128, True)
         assert p["persistent"] == int(c["persistent"]), c
-        assert p["grid"] == (256 if c["persistent"] else p["work_items"])
+        if c["persistent"]:
+            assert p["grid"] == 256 and p["split_tiles"] == 0
+        else:  # one workgroup per item, or per part of an item when keys are split
+            assert p["grid"] == (p["work_items"] if p["split_tiles"] == 0 else
+                                 _split_parts(p, c["B"], c["Hq"], c["Sq"], c["Sq"], True,
+                                              p["split_tiles"]))
+
+
+def _block_tiles(p, Sq, Sk, causal):
+    """KV tiles of every query block, from the mask by brute force."""
+    BM, BN = p["block_m"], p["block_n"]
+    out = []
+    for q0 in range(0, Sq, BM):
+        last = min(Sq, q0 + BM) - 1
+        kv_end = min(max(last + 1 + Sk - Sq, 0), Sk) if causal else Sk
+        out.append(-(-kv_end // BN))
+    return out
+
+
+def _split_parts(p, B, Hq, Sq, Sk, causal, T):
+    return B * Hq * sum(max(1, -(-nt // T)) for nt in _block_tiles(p, Sq, Sk, causal))
+
+
+def test_split_plan_brute_force():
+    # under-filled launches (fewer items than the 256 CUs): the smallest
+    # tiles-per-part T >= 2 whose parts fit 256 workgroups, taken when it cuts
+    # the longest item by at least 2 tiles
+    for (B, Hq, Sq, Sk, causal) in [(1, 16, 2048, 2048, True), (1, 16, 2048, 2048, False),
+                                    (1, 128, 256, 256, True), (1, 2, 256, 256, True),
+                                    (2, 8, 1000, 3000, True), (1, 4, 300, 9000, False),
+                                    (1, 1, 8192, 8192, True), (1, 3, 700, 100, True),
+                                    (1, 64, 64, 65536, True), (1, 32, 512, 512, False)]:
+        p = fa.fwd_plan(B, Hq, Hq, Sq, Sk, 128, causal)
+        if p["persistent"]:
+            assert p["split_tiles"] == 0
+            continue
+        nts = _block_tiles(p, Sq, Sk, causal)
+        max_nt = max(nts)
+        T = next((t for t in range(2, max_nt + 1)
+                  if _split_parts(p, B, Hq, Sq, Sk, causal, t) <= 256), None)
+        if T is not None and T <= max_nt - 2:
+            assert p["split_tiles"] == T, (B, Hq, Sq, Sk, causal)
+            assert p["grid"] == _split_parts(p, B, Hq, Sq, Sk, causal, T) <= 256
+        else:
+            assert p["split_tiles"] == 0 and p["grid"] == p["work_items"], (B, Hq, Sq, Sk, causal)
+    # the MHA 2048 shapes: 16 heads x 8 query blocks = 128 items
+    assert fa.fwd_plan(1, 16, 16, 2048, 2048, 128, True)["split_tiles"] == 6
+    assert fa.fwd_plan(1, 16, 16, 2048, 2048, 128, False)["split_tiles"] == 8
+    assert fa.fwd_plan(1, 16, 16, 2048, 2048, 128, False)["grid"] == 256
 
 
 def test_plan_tile_counts_brute_force():

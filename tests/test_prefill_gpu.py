@@ -309,8 +309,82 @@ def test_persistent_and_grid_launches_agree_bitwise():
     for pers, hkv, xcd in ((0, 0, 0), (0, 1, 0), (1, 0, 0), (1, 1, 0), (1, 0, 1), (1, 1, 1)):
         sched = dict(persistent=pers, hkv_major=hkv, xcd_map=xcd)
         outs.append(bits_of(fa.fwd(tq, tk, tv, causal=True, scale=0.088, schedule=sched)))
+    # the key-split launch with parts of up to 8 tiles: every item here has at
+    # most 1024 / 128 = 8 tiles, so each part is a whole item -- the split
+    # launch's own mapping of workgroups to items, with nothing to merge
+    sched = dict(persistent=0, hkv_major=0, xcd_map=0, split_tiles=8)
+    outs.append(bits_of(fa.fwd(tq, tk, tv, causal=True, scale=0.088, schedule=sched)))
     for o in outs[1:]:
         assert np.array_equal(outs[0], o)
+
+
+# B, Hq, Hkv, Sq, Sk, D, causal, dtype, tiles per part
+SPLITS = [
+    (1, 4, 2, 700, 300, 128, True, "bf16", 1),    # Sq > Sk: rows without keys; 1 tile a part
+    (2, 4, 1, 257, 700, 64, True, "bf16", 1),     # bottom-right ragged, 6 parts an item
+    (1, 3, 3, 511, 513, 128, False, "fp16", 2),   # 5 tiles (one key in the last) in 3 parts
+    (1, 16, 1, 65, 1000, 128, True, "bf16", 3),   # 8 tiles cut 2 + 3 + 3
+    (1, 2, 1, 300, 2000, 128, False, "bf16", 5),  # 16 tiles in 4 parts, ragged key tail
+]
+
+
+@pytest.mark.parametrize("case", SPLITS, ids=[str(c) for c in SPLITS])
+def test_key_split_matches_oracle_and_repeats_bitwise(case):
+    # each item's keys cut into parts summed by separate workgroups and merged
+    # by the last part: O and LSE against the oracle, the same bits on a
+    # second call, and within rounding of the unsplit launch
+    B, Hq, Hkv, Sq, Sk, D, causal, dtype, T = case
+    print(f"\n[prefill split] {case}", flush=True)
+    fa = _fa()
+    q, k, v = shape_inputs(B, Hq, Hkv, Sq, Sk, D, dtype, seed=400 + 10 * SPLITS.index(case))
+    tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    scale = 1.0 / math.sqrt(D)
+    sched = dict(persistent=0, hkv_major=0, xcd_map=0, split_tiles=T)
+    o1, l1 = fa.fwd(tq, tk, tv, causal=causal, scale=scale, return_lse=True, schedule=sched)
+    o2, l2 = fa.fwd(tq, tk, tv, causal=causal, scale=scale, return_lse=True, schedule=sched)
+    a, b = bits_of(o1), bits_of(o2)
+    assert np.array_equal(a, b)
+    assert np.array_equal(l1.cpu().numpy().view(np.uint32), l2.cpu().numpy().view(np.uint32))
+    qf, kf, vf = oracle.widen(q, dtype), oracle.widen(k, dtype), oracle.widen(v, dtype)
+    got = oracle.widen(a, dtype)
+    ref_o = oracle.attention_ref(qf, kf, vf, causal, scale)
+    st = parity(got, ref_o, str(case))
+    print(f"  {st}", flush=True)
+    ref = oracle.lse_ref(qf, kf, causal, scale)
+    lse = l1.cpu().numpy().astype(np.float64)
+    fin = np.isfinite(ref)
+    assert np.array_equal(np.isfinite(lse), fin)
+    assert np.all(np.isneginf(lse[~fin]))
+    np.testing.assert_allclose(lse[fin], ref[fin], rtol=1e-4, atol=1e-3)
+    if causal and Sq > Sk:
+        assert np.all(got[:, :, :Sq - Sk] == 0)
+    plain = oracle.widen(bits_of(fa.fwd(tq, tk, tv, causal=causal, scale=scale,
+                                        schedule=dict(persistent=0, hkv_major=0, xcd_map=0))),
+                         dtype)
+    # the split changes rounding only (each part's own reference max rounds
+    # exp2 and the packed P differently; the merge adds in another order):
+    # its worst error against the oracle stays within twice the unsplit
+    # launch's, plus half a bf16 unit at 1
+    e_split = float(np.max(np.abs(got - ref_o)))
+    e_plain = float(np.max(np.abs(plain - ref_o)))
+    print(f"  max |err| split {e_split:.2e}, unsplit {e_plain:.2e}", flush=True)
+    assert e_split <= 2 * e_plain + 2.0 ** -8
+
+
+def test_key_split_workspace_reused_across_shapes():
+    # split launches of different shapes and part counts in a row on one
+    # stream share the workspace: each leaves its counters at zero, so the
+    # first shape gives the same bits again afterwards
+    fa = _fa()
+    dtype = "bf16"
+    runs = []
+    for (B, Hq, Hkv, Sq, Sk, D, T) in ((1, 16, 1, 65, 1000, 128, 3), (2, 4, 2, 300, 1500, 64, 1),
+                                       (1, 16, 1, 65, 1000, 128, 3)):
+        q, k, v = shape_inputs(B, Hq, Hkv, Sq, Sk, D, dtype, seed=450 + Sk)
+        tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+        sched = dict(persistent=0, hkv_major=0, xcd_map=0, split_tiles=T)
+        runs.append(bits_of(fa.fwd(tq, tk, tv, causal=True, scale=0.1, schedule=sched)))
+    assert np.array_equal(runs[0], runs[2])
 
 
 def test_planned_rejects_schedules_that_do_not_fit():
