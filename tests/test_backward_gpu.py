@@ -106,3 +106,24 @@ def test_backward_many_tiles_gqa4():
                                    1 / math.sqrt(D))
     for name, a, r in zip(("dq", "dk", "dv"), got, ref):
         grad_parity(a, r, f"{name} S=2048 gqa4")
+
+
+@pytest.mark.parametrize("case", [(1, 8, 1, 4096, 4096, 128, True),
+                                  (1, 16, 2, 1000, 4500, 64, True),
+                                  (1, 8, 1, 4096, 4096, 128, False)],
+                         ids=["s4096_gqa8_causal", "sq1000_sk4500_gqa8_d64", "s4096_gqa8_full"])
+def test_backward_long_keys_gqa8(case):
+    # dK / dV summed over an 8-head GQA group and over 4096+ keys: 32+ dk/dv
+    # key blocks, each accumulating the contributions of every query block
+    # and of all 8 query heads of its kv head (the full oracle backward,
+    # a few seconds of float64 on the host)
+    B, Hq, Hkv, Sq, Sk, D, causal = case
+    dtype = "bf16"
+    print(f"\n[backward] {case}", flush=True)
+    q, k, v, g = (wl.normal_bits(sh, 1500 + i, dtype) for i, sh in
+                  enumerate([(B, Hq, Sq, D), (B, Hkv, Sk, D), (B, Hkv, Sk, D), (B, Hq, Sq, D)]))
+    scale = 1 / math.sqrt(D)
+    got = run_bwd(q, k, v, g, causal, scale, dtype)
+    ref = oracle.attention_bwd_ref(*(oracle.widen(x, dtype) for x in (q, k, v, g)), causal, scale)
+    fr = [grad_parity(a, r, f"{name} {case}") for name, a, r in zip(("dq", "dk", "dv"), got, ref)]
+    print(f"  worst fraction of bound dq {fr[0]:.3f} dk {fr[1]:.3f} dv {fr[2]:.3f}", flush=True)
