@@ -12,9 +12,13 @@
 //  * in persistent mode a grid of one workgroup per CU strides over the
 //    items ("Persistent (grid-stride) mode"), ordered kv-head-major when
 //    that still balances, so concurrently running items share K/V in L2;
-//  * KV tiles of 64 keys stream through rings of three row-padded LDS
-//    slots ("Baked-in levers": K rows padded against bank conflicts, V pad),
-//    copied by 16-byte buffer loads that write LDS directly;
+//  * with fewer items than CUs, each item's key tiles may be cut into parts
+//    run by separate workgroups, whose partial (O, max, sum) the last part
+//    to start merges in the same launch (merge_parts);
+//  * KV tiles of kPrefillBN keys (128; 64 as a build option) stream through
+//    rings of two (three) row-padded LDS slots ("Baked-in levers": K rows
+//    padded against bank conflicts, V pad), copied by 16-byte buffer loads
+//    that write LDS directly;
 //  * the two waves that share a SIMD run one phase apart (ping-pong): while
 //    one issues the tile's MFMAs the other runs its softmax;
 //  * below-diagonal tiles run mask-free, only tiles crossing the diagonal
@@ -423,6 +427,83 @@ void prefill_kernel(PrefillParams p) {
   // and its arrival rank among the item's parts (through LDS)
   int part = 0, nparts = 1, t0 = 0, t1 = 0;
   __shared__ unsigned split_word[SPLIT ? 2 : 1];
+
+  // Where an item's rows and keys live: its sequence has Sq query rows and Sk
+  // keys, row strides QRS / KRS elements.  Dense: [B, H, S, D] tensors.
+  // Varlen: packed [total, H, D] tensors whose sequence b spans rows
+  // [cu[b], cu[b + 1]), with offsets clamped to [0, total] and lengths to the
+  // declared maxima (p.Sq, p.Sk), so no index leaves the tensors whatever the
+  // offsets hold.  False for a varlen query block past its sequence's end.
+  struct ItemLoc {
+    int b, hq, q0, Sq, Sk, q_lo, QRS, KRS;
+    long long qbase, kvbase;
+  };
+  auto locate = [&](int w, ItemLoc& L) -> bool {
+    int b, hq, qb;
+    if (compact) varlen_item(p, nqb_tab, total_blocks, w, lane, xmap, xcd, b, hq, qb);
+    else if (xmap) xcd_item(p, xcd, w, b, hq, qb);
+    else decode_item(p, w, b, hq, qb);
+    const int hk = hq / p.gqa;
+    L.b = b;
+    L.hq = hq;
+    L.q0 = qb * BM;
+    L.Sq = p.Sq;
+    L.Sk = p.Sk;
+    L.q_lo = 0;
+    L.QRS = D;
+    L.KRS = D;
+    if constexpr (VARLEN) {
+      int q_lo = min(max(p.cu_q[b], 0), p.total_q);
+      const int q_hi = min(max(p.cu_q[b + 1], q_lo), p.total_q);
+      const int k_lo = min(max(p.cu_k[b], 0), p.total_k);
+      const int k_hi = min(max(p.cu_k[b + 1], k_lo), p.total_k);
+      L.Sq = uniform(min(q_hi - q_lo, p.Sq));
+      L.Sk = uniform(min(k_hi - k_lo, p.Sk));
+      q_lo = uniform(q_lo);
+      L.q_lo = q_lo;
+      L.QRS = p.Hq * D;
+      L.KRS = p.Hkv * D;
+      L.qbase = (long long)q_lo * L.QRS + (long long)hq * D;
+      L.kvbase = (long long)uniform(k_lo) * L.KRS + (long long)hk * D;
+      return L.q0 < L.Sq;
+    } else {
+      L.qbase = (long long)b * p.q_bstride + (long long)hq * L.Sq * D;
+      L.kvbase = (long long)b * p.kv_bstride + (long long)hk * L.Sk * D;
+      return true;
+    }
+  };
+  // Q rows of this wave as the B operand, lane holding q[row][16kk + 8lh ..
+  // +7], as raw bits: buffer loads from a range that ends after the item's
+  // last row, so rows past it read zeros without a branch, and nothing waits
+  // for the loads here (the sign of the scale is folded in by fold_q once
+  // they have landed)
+  u32x4 qr[KSTEPS];
+  auto load_q = [&](const ItemLoc& L) {
+    const int rows = min(BM, L.Sq - L.q0);
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(qg + L.qbase + (long long)L.q0 * L.QRS), (short)0,
+        ((rows - 1) * L.QRS + D) * 2, kBufferFlags);
+#pragma unroll
+    for (int kk = 0; kk < KSTEPS; ++kk)
+      qr[kk] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     qrs, ((wave * 32 + li) * L.QRS + 16 * kk + 8 * lh) * 2, 0, 0));
+  };
+  auto fold_q = [&]() {
+    if (p.q_sign != 1) {
+#pragma unroll
+      for (int kk = 0; kk < KSTEPS; ++kk)
+        qr[kk] = p.q_sign < 0 ? (qr[kk] ^ 0x80008000u) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  // Cross-item prefetch (persistent grids, two-slot rings): in its last
+  // phases an item loads the next item's Q and copies its first K/V tile,
+  // each wave group into the ring slot it would fill with the item's own
+  // tile ntiles, so the next item starts without a prologue.  The ring numbering carries
+  // on across items: tile t of an item sits in slot (t + ring) % NBUF.
+  constexpr bool kPrefetch = NBUF == 2 && !SPLIT;
+  bool have_pf = false;  // this item's Q and tile 0 were loaded by the one before
+  int ring = 0;
   for (int round = 0;; ++round) {
     int w;
     if (p.persistent) {
@@ -440,39 +521,15 @@ void prefill_kernel(PrefillParams p) {
       }
       if (w >= work_items) break;
     }
-    int b, hq, qb;
-    if (compact) varlen_item(p, nqb_tab, total_blocks, w, lane, xmap, xcd, b, hq, qb);
-    else if (xmap) xcd_item(p, xcd, w, b, hq, qb);
-    else decode_item(p, w, b, hq, qb);
-    const int hk = hq / p.gqa;
-    const int q0 = qb * BM;
+    ItemLoc L;
+    if (!locate(w, L)) continue;  // query block past the end of this sequence
+    const int b = L.b, hq = L.hq, q0 = L.q0, QRS = L.QRS, KRS = L.KRS;
+    int Sq = L.Sq, Sk = L.Sk;
+    const int q_lo = L.q_lo;
+    const long long qbase = L.qbase;
+    long long kvbase = L.kvbase;
     const int rw0 = q0 + wave * 32;  // first row of this wave
     const int row = rw0 + li;        // this lane's query row
-    // this item's sequence: Sq query rows and Sk keys, row strides QRS / KRS
-    // elements.  Dense: [B, H, S, D] tensors.  Varlen: packed [total, H, D]
-    // tensors whose sequence b spans rows [cu[b], cu[b + 1]), with offsets
-    // clamped to [0, total] and lengths to the declared maxima (p.Sq, p.Sk),
-    // so no index leaves the tensors whatever the offsets hold.
-    int Sq = p.Sq, Sk = p.Sk, q_lo = 0;
-    long long qbase, kvbase;
-    int QRS = D, KRS = D;
-    if constexpr (VARLEN) {
-      q_lo = min(max(p.cu_q[b], 0), p.total_q);
-      const int q_hi = min(max(p.cu_q[b + 1], q_lo), p.total_q);
-      const int k_lo = min(max(p.cu_k[b], 0), p.total_k);
-      const int k_hi = min(max(p.cu_k[b + 1], k_lo), p.total_k);
-      Sq = uniform(min(q_hi - q_lo, p.Sq));
-      Sk = uniform(min(k_hi - k_lo, p.Sk));
-      q_lo = uniform(q_lo);
-      QRS = p.Hq * D;
-      KRS = p.Hkv * D;
-      qbase = (long long)q_lo * QRS + (long long)hq * D;
-      kvbase = (long long)uniform(k_lo) * KRS + (long long)hk * D;
-      if (q0 >= Sq) continue;  // query block past the end of this sequence
-    } else {
-      qbase = (long long)b * p.q_bstride + (long long)hq * Sq * D;
-      kvbase = (long long)b * p.kv_bstride + (long long)hk * Sk * D;
-    }
     int kv_off = Sk - Sq;  // bottom-right causal offset
 
     // keys [0, kv_end) are streamed for the item; this wave needs [0, wave_end)
@@ -504,16 +561,6 @@ void prefill_kernel(PrefillParams p) {
     }
     main_tiles = min(main_tiles, ntiles);
 
-    // Q rows of this wave as the B operand: lane holds q[row][16kk + 8lh .. +7]
-    u32x4 qr[KSTEPS];
-#pragma unroll
-    for (int kk = 0; kk < KSTEPS; ++kk) {
-      u32x4 x = {0u, 0u, 0u, 0u};
-      if (row < Sq) x = gload16(qg + qbase + (long long)row * QRS + 16 * kk + 8 * lh);
-      if (p.q_sign < 0) x ^= 0x80008000u;
-      if (p.q_sign == 0) x = u32x4{0u, 0u, 0u, 0u};
-      qr[kk] = x;
-    }
 
     f32x16 oacc[DTILES];
 #pragma unroll
@@ -629,19 +676,20 @@ void prefill_kernel(PrefillParams p) {
 
     // ---- ping-pong schedule ----------------------------------------------------
     // Each wave runs the step sequence M(0) V(0) M(1) V(1) ... M(ntiles) over
-    // its 64-key tiles:
-    //   M(t): S_t = K_t Q^T, then O^T += V_{t-1}^T P_{t-1}^T   (BN / 2 MFMAs)
+    // its BN-key tiles:
+    //   M(t): S_t = K_t Q^T, then O^T += V_{t-1}^T P_{t-1}^T
     //   V(t): mask (diagonal / tail only), online softmax of S_t -> P_t
     // The two waves that share a SIMD run the sequence one phase apart (waves
     // 0-3 lead, 4-7 follow): while one issues MFMAs the other runs its softmax
     // on the vector unit.  Every phase ends with a workgroup barrier.  LDS
-    // holds rings of three K and three V tiles: K(t) is read in phases 2t,
-    // 2t+1 and V(t) in 2t+2, 2t+3, so K(X) written in phase 2X-3 and V(X) in
-    // phase 2X-2 never overwrite a tile still being read.
+    // holds rings of NBUF K and NBUF V tiles: K(t) is read in phases 2t,
+    // 2t+1 and V(t) in 2t+2, 2t+3, so K(X) copied in phase 2X - 2 NBUF + 3
+    // and V(X) in phase 2X - 2 NBUF + 4 land after the last read of the tile
+    // that held their slot and before the barrier ahead of their first read.
     // ring slot of a tile; readfirstlane keeps it a per-phase scalar instead
     // of letting strength reduction turn every LDS address into a live
     // induction register
-    auto slot = [](int tile) { return uniform(tile % NBUF); };
+    auto slot = [&](int tile) { return uniform((tile + ring) % NBUF); };
     // tile t is needed by this wave iff t*BN < wave_end; sub-tile keys past
     // free_keys need the mask for some row of this wave
     int free_keys = Sk;
@@ -663,20 +711,42 @@ void prefill_kernel(PrefillParams p) {
 #pragma unroll
     for (int u = 0; u < kDmaSlots; ++u) dma_offs[u] = dma_offset(lead ? KRC : VRC, u);
 
-    // prologue: the leading group copies K of tiles 0 .. NBUF - 2, the
-    // following group V of the same tiles
-    if (lead) {
-      dma_tile(krs, Ks, 0, KNI, dma_offs);
-      if (NBUF > 2 && ntiles > 1) dma_tile(krs, Ks + slot(1) * KTILE, 1, KNI, dma_offs);
-    } else {
-      dma_tile(vrs, Vs, 0, VNI, dma_offs);
-      if (NBUF > 2 && ntiles > 1) dma_tile(vrs, Vs + slot(1) * VTILE, 1, VNI, dma_offs);
+    // prologue (unless the item before loaded it): Q, and the leading group
+    // copies K of tiles 0 .. NBUF - 2, the following group V of the same tiles
+    if (!have_pf) {
+      load_q(L);
+      if (lead) {
+        dma_tile(krs, Ks + slot(0) * KTILE, 0, KNI, dma_offs);
+        if (NBUF > 2 && ntiles > 1) dma_tile(krs, Ks + slot(1) * KTILE, 1, KNI, dma_offs);
+      } else {
+        dma_tile(vrs, Vs + slot(0) * VTILE, 0, VNI, dma_offs);
+        if (NBUF > 2 && ntiles > 1) dma_tile(vrs, Vs + slot(1) * VTILE, 1, VNI, dma_offs);
+      }
+    }
+    // the next item of this workgroup, prefetched in this item's last phases
+    ItemLoc N;
+    bool pf = false;
+    __amdgpu_buffer_rsrc_t krs_n = krs, vrs_n = vrs;
+    if constexpr (kPrefetch) {
+      const int nr = round + 1;
+      if (p.persistent && ntiles > 0 && nr * NP < list_items) {
+        const int wn = nr * NP + ((nr & 1) ? (NP - 1 - cta) : cta);
+        if (wn < list_items && locate(wn, N)) {
+          pf = true;
+          const int nb = N.Sk > 0 ? ((N.Sk - 1) * N.KRS + D) * 2 : 0;
+          krs_n = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kg + N.kvbase), (short)0,
+                                                    nb, kBufferFlags);
+          vrs_n = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vg + N.kvbase), (short)0,
+                                                    nb, kBufferFlags);
+        }
+      }
     }
     if constexpr (SPLIT) {
       if (nparts > 1 && tid == 0) split_word[0] = add_flag(p.split_cnt + 2 * w, 1u);
     }
     wait_vmem();
     __syncthreads();
+    fold_q();
 
     auto run = [&](auto lag_c) {
       constexpr int LAG = decltype(lag_c)::value;
@@ -687,9 +757,17 @@ void prefill_kernel(PrefillParams p) {
       auto needed = [&](int t) { return t >= 0 && t < ntiles && t * BN < wave_end; };
       // one phase of kind KIND (0: M step, 1: V step) for this wave; ALL: every
       // operation of the step is known to be needed and mask-free
-      auto phase = [&](int g, auto kind_c, auto all_c) {
+      auto phase = [&](int g, auto kind_c, auto all_c, auto last_c) {
         constexpr int KIND = decltype(kind_c)::value;
         constexpr bool ALL = decltype(all_c)::value;
+        // LAST: one of the final two phases (2 ntiles, 2 ntiles + 1), which
+        // have no QK product (there is no tile ntiles), so Q is free: the
+        // first of them loads the next item's Q, ahead of the next item's
+        // K/V copies that the following group issues in the same phase
+        constexpr bool LAST = decltype(last_c)::value;
+        if constexpr (LAST && kPrefetch) {
+          if (pf && g == nphase - 2) load_q(N);
+        }
         // the leading group copies K(X) in its V phase 2X - 2 NBUF + 3, the
         // following group V(X) in its V phase 2X - 2 NBUF + 4 (tiles below
         // NBUF - 1 come with the prologue): the slot it fills was last read
@@ -705,6 +783,15 @@ void prefill_kernel(PrefillParams p) {
         if (do_load) {
           if (LAG == 0) dma_tile(krs, Ks + slot(Xld) * KTILE, Xld, KNI, dma_offs);
           else dma_tile(vrs, Vs + slot(Xld) * VTILE, Xld, VNI, dma_offs);
+        }
+        if constexpr (KIND == 1 && kPrefetch && !ALL) {
+          // this group's last V phase: the slot of tile ntiles was last read
+          // a phase ago.  Nothing waits for the copy until the next item
+          // starts.
+          if (pf && Xld == ntiles) {
+            if (LAG == 0) dma_tile(krs_n, Ks + slot(Xld) * KTILE, 0, KNI, dma_offs);
+            else dma_tile(vrs_n, Vs + slot(Xld) * VTILE, 0, VNI, dma_offs);
+          }
         }
         const int sidx = g - LAG;
         const int t = sidx >> 1;
@@ -723,13 +810,15 @@ void prefill_kernel(PrefillParams p) {
             m_step(std::integral_constant<int, NST * 2 * DTILES>{}, std::integral_constant<int, 0>{},
                    Vb, Ks, P, S);
           }
-          if (sidx >= 0 && needed(t)) {
-            const uint16_t* Kb = Ks + slot(t) * KTILE;
-            m_step(std::integral_constant<int, 0>{}, std::integral_constant<int, NST * KSTEPS>{},
-                   Vs, Kb, P, S);
+          if constexpr (!LAST) {
+            if (sidx >= 0 && needed(t)) {
+              const uint16_t* Kb = Ks + slot(t) * KTILE;
+              m_step(std::integral_constant<int, 0>{}, std::integral_constant<int, NST * KSTEPS>{},
+                     Vs, Kb, P, S);
+            }
           }
         } else if (ALL || (sidx >= 0 && needed(t))) {
-          // V(t): mask and softmax of the 64 keys of tile t
+          // V(t): mask and softmax of the BN keys of tile t
           if (!ALL && t * BN + BN > free_keys) {
             // register r of S[st] holds key t*BN + 32 st + 4*lh + off(r): keep
             // keys <= lim = min(row + Sk - Sq, Sk - 1) of this lane's row
@@ -760,23 +849,33 @@ void prefill_kernel(PrefillParams p) {
       // phase g runs step g - LAG: an M step when it is even, a V step when odd
       using K0 = std::integral_constant<int, LAG>;      // kind of even phases
       using K1 = std::integral_constant<int, 1 - LAG>;  // kind of odd phases
+      using F = std::false_type;
+      using T = std::true_type;
       int g = 0;
-      for (; g + 1 < min(4, nphase); g += 2) {
-        phase(g, K0{}, std::false_type{});
-        phase(g + 1, K1{}, std::false_type{});
+      for (; g + 1 < min(4, nphase - 2); g += 2) {
+        phase(g, K0{}, F{}, F{});
+        phase(g + 1, K1{}, F{}, F{});
       }
       for (; g + 1 < main_end; g += 2) {
-        phase(g, K0{}, std::true_type{});
-        phase(g + 1, K1{}, std::true_type{});
+        phase(g, K0{}, T{}, F{});
+        phase(g + 1, K1{}, T{}, F{});
       }
-      for (; g + 1 < nphase; g += 2) {
-        phase(g, K0{}, std::false_type{});
-        phase(g + 1, K1{}, std::false_type{});
+      for (; g + 1 < nphase - 2; g += 2) {
+        phase(g, K0{}, F{}, F{});
+        phase(g + 1, K1{}, F{}, F{});
+      }
+      if (nphase > 0) {
+        phase(nphase - 2, K0{}, F{}, T{});
+        phase(nphase - 1, K1{}, F{}, T{});
       }
     };
     if (wave < kPrefillWaves / 2) run(std::integral_constant<int, 0>{});
     else run(std::integral_constant<int, 1>{});
     (void)free_tiles;
+    if constexpr (kPrefetch) {
+      have_pf = pf;
+      ring = uniform((ring + ntiles) % NBUF);
+    }
 
     // ---- epilogue: O = O^T / l, rows < Sq --------------------------------------
     float l_tot = pair_sum(l_run);
