@@ -61,7 +61,8 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, ret
     Bottom-right aligned causal mask when causal=True.  scale defaults to
     1/sqrt(D).  With return_lse=True also returns the fp32 row log-sum-exp
     [B,Hq,Sq].  `schedule` (keys persistent, hkv_major, xcd_map, each 0/1,
-    and optionally split_tiles >= 0) overrides the automatic launch schedule
+    and optionally queue 0/1 and split_tiles >= 0) overrides the automatic
+    launch schedule
     (fa_fwd_planned); without a split the result is bitwise the same, with
     one it differs by rounding only."""
     torch = _torch()
@@ -87,6 +88,7 @@ def fwd(q, k, v, causal: bool = False, scale: float | None = None, out=None, ret
         for key in ("persistent", "hkv_major", "xcd_map"):
             setattr(plan, key, int(schedule[key]))
         plan.split_tiles = int(schedule.get("split_tiles", 0))
+        plan.queue = int(schedule.get("queue", 0))
         lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=dev) if return_lse else None
         st = lib().fa_fwd_planned(q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
                                   lse.data_ptr() if lse is not None else None, B, Hq, Hkv, Sq, Sk,

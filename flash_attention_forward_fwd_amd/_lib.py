@@ -52,7 +52,8 @@ class FwdPlan(ctypes.Structure):
                 ("work_items", ctypes.c_int), ("grid", ctypes.c_int),
                 ("persistent", ctypes.c_int), ("hkv_major", ctypes.c_int),
                 ("kv_tiles", ctypes.c_longlong), ("masked_tiles", ctypes.c_longlong),
-                ("xcd_map", ctypes.c_int), ("split_tiles", ctypes.c_int)]
+                ("xcd_map", ctypes.c_int), ("split_tiles", ctypes.c_int),
+                ("queue", ctypes.c_int)]
 
 
 _lib = None

@@ -109,6 +109,8 @@ fa_status_t plan_prefill(int B, int Hq, int Hkv, int Sq, int Sk, int D, int caus
                       ((long long)B * Hkv) % fa::kXcds == 0;
   plan->hkv_major = hkv;
   plan->xcd_map = (xcd_ok && !hkv) ? 1 : 0;
+  // work queue for every persistent launch (items dealt to free workgroups)
+  plan->queue = persistent;
   // tiles streamed and tiles needing the mask, per query block (x Hq*B)
   long long tiles = 0, masked = 0;
   const long long off = (long long)Sk - Sq;
@@ -163,16 +165,17 @@ fa_status_t apply_plan(const fa_fwd_plan_t* want, fa_fwd_plan_t* plan, int B, in
                        int Sq, int Sk, int causal) {
   if ((want->persistent != 0 && want->persistent != 1) ||
       (want->hkv_major != 0 && want->hkv_major != 1) || (want->xcd_map != 0 && want->xcd_map != 1) ||
-      want->split_tiles < 0)
+      (want->queue != 0 && want->queue != 1) || want->split_tiles < 0)
     return FA_ERR_SHAPE;
   if (want->split_tiles > 0) {
-    if (want->persistent || want->hkv_major || want->xcd_map) return FA_ERR_SHAPE;
+    if (want->persistent || want->hkv_major || want->xcd_map || want->queue) return FA_ERR_SHAPE;
     const long long parts = split_parts(B, Hq, Sq, Sk, causal, want->split_tiles);
     if (parts > fa::kSplitMaxParts) return FA_ERR_SHAPE;
     plan->persistent = 0;
     plan->grid = (int)parts;
     plan->hkv_major = 0;
     plan->xcd_map = 0;
+    plan->queue = 0;
     plan->split_tiles = want->split_tiles;
     return FA_OK;
   }
@@ -183,16 +186,19 @@ fa_status_t apply_plan(const fa_fwd_plan_t* want, fa_fwd_plan_t* plan, int B, in
   if (want->xcd_map && !(persistent && grid == NP && NP % fa::kXcds == 0 &&
                          ((long long)B * Hkv) % fa::kXcds == 0))
     return FA_ERR_SHAPE;
+  if (want->queue && !persistent) return FA_ERR_SHAPE;
   plan->persistent = persistent;
   plan->grid = grid;
   plan->hkv_major = want->hkv_major;
   plan->xcd_map = want->xcd_map;
+  plan->queue = want->queue;
   return FA_OK;
 }
 
-// Key-split workspace, one per (device, stream): counters (zeroed here once;
-// every split launch leaves them at zero) and the part records.  Kept until
-// the process ends, as a stream's launches may still be in flight.
+// Prefill workspace, one per (device, stream): the split and work-queue
+// counters (zeroed here once; every launch leaves them at zero) and the split
+// part records.  Kept until the process ends, as a stream's launches may
+// still be in flight.
 struct SplitWorkspace {
   int device;
   void* stream;
@@ -278,11 +284,13 @@ fa_status_t fwd_impl(const void* q, const void* k, const void* v, void* o, float
   p.split_tiles = plan.split_tiles;
   p.split_cnt = nullptr;
   p.split_rec = nullptr;
-  if (plan.split_tiles > 0) {
+  p.queue = nullptr;
+  if (plan.split_tiles > 0 || plan.queue) {
     void* ws = nullptr;
     if (split_workspace(stream, &ws) != hipSuccess) return FA_ERR_HIP;
     p.split_cnt = static_cast<unsigned*>(ws);
     p.split_rec = reinterpret_cast<float*>(static_cast<char*>(ws) + fa::kSplitCounterBytes);
+    if (plan.queue) p.queue = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + fa::kQueueOffset);
   }
   const hipError_t e = fa::launch_prefill(p, D, dtype, causal != 0, plan.grid,
                                           static_cast<hipStream_t>(stream));
@@ -363,6 +371,12 @@ fa_status_t launch_varlen(const void* q, const void* k, const void* v, void* o, 
   p.split_tiles = 0;
   p.split_cnt = nullptr;
   p.split_rec = nullptr;
+  p.queue = nullptr;
+  if (plan.queue) {
+    void* ws = nullptr;
+    if (split_workspace(stream, &ws) != hipSuccess) return FA_ERR_HIP;
+    p.queue = reinterpret_cast<unsigned*>(static_cast<char*>(ws) + fa::kQueueOffset);
+  }
   const hipError_t e = fa::launch_prefill(p, D, dtype, causal != 0, plan.grid,
                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? FA_OK : FA_ERR_HIP;

@@ -33,9 +33,14 @@ constexpr int kXcds = 8;
 // part, and the item's last part to finish merges the others' partial results.
 constexpr int kSplitMinTiles = 2;      // a part holds at least this many tiles
 constexpr int kSplitMaxParts = kNumCUs; // workgroups of a split launch at most
-// per-item counters (arrivals, records written), then the part records
+// Workspace of a (device, stream): the split launches' per-item counters
+// (arrivals, records written) and the persistent launches' work-queue
+// counters (one ticket counter per item list, then a finished-workgroup
+// counter), all zero between launches, then the split part records.
 constexpr size_t kSplitCounterBytes = 4096;
-static_assert(kSplitMaxParts * 2 * sizeof(unsigned) <= kSplitCounterBytes, "counters fit");
+constexpr size_t kQueueOffset = 2048;  // bytes from the workspace start
+static_assert(kSplitMaxParts * 2 * sizeof(unsigned) <= kQueueOffset, "split counters fit");
+static_assert(kQueueOffset + 16 * sizeof(unsigned) <= kSplitCounterBytes, "queue counters fit");
 // fp32 record of one part: per wave and lane D/2 O values, then (m, l)
 constexpr size_t split_record_bytes(int D) { return (size_t)kPrefillWaves * 64 * (D / 2 + 2) * 4; }
 constexpr size_t kSplitWorkspaceBytes = kSplitCounterBytes + kSplitMaxParts * split_record_bytes(128);
@@ -76,6 +81,11 @@ struct PrefillParams {
   int split_tiles;
   unsigned* split_cnt;
   float* split_rec;
+  // persistent launches: nullptr for the static round-robin over the item
+  // list, else the work-queue counters (kXcds ticket counters, then the
+  // finished-workgroup counter) that hand out items after each workgroup's
+  // first
+  unsigned* queue;
 };
 
 hipError_t launch_prefill(const PrefillParams& p, int D, int dtype, bool causal, int grid,

@@ -504,9 +504,34 @@ void prefill_kernel(PrefillParams p) {
   constexpr bool kPrefetch = NBUF == 2 && !SPLIT;
   bool have_pf = false;  // this item's Q and tile 0 were loaded by the one before
   int ring = 0;
+  // Work queue (persistent launches with the prefetch): a workgroup's first
+  // item is its own index in its list; each later item is list position
+  // NP + t for a ticket t taken from the list's counter.  The ticket for the
+  // item after next is taken in an item's final phase, so the next item is
+  // known (and prefetched) a whole item ahead and the atomic's latency hides
+  // behind the item's end.  Items are dealt in list order (heaviest first
+  // within each kv head), each to the first workgroup that is free, which
+  // also evens out XCDs that run at different speeds.  The queue state lives
+  // in LDS, not in registers, which the tile loop needs every one of:
+  // q_item[r & 1] holds round r's item, q_tick the ticket thread 0 took in
+  // the last item (kEmpty if that item ran no phase and took none).
+  const bool qmode = kPrefetch && p.persistent && p.queue != nullptr;
+  __shared__ unsigned q_item[2], q_tick;
+  constexpr unsigned kEmpty = 0xFFFFFFFFu, kNoTicket = 0x3FFFFFFFu;
+  auto qctr = [&]() { return p.queue + (xmap ? xcd : 0); };
   for (int round = 0;; ++round) {
     int w;
-    if (p.persistent) {
+    if (qmode) {
+      w = round == 0 ? cta : uniform((int)q_item[round & 1]);
+      if (tid == 0) {
+        unsigned t = round == 0 ? kEmpty : q_tick;
+        if (t == kEmpty) t = add_flag(qctr(), 1u);
+        q_item[(round + 1) & 1] = NP + min(t, kNoTicket);
+        q_tick = kEmpty;
+      }
+      __syncthreads();
+      if (w >= list_items) break;
+    } else if (p.persistent) {
       if (round * NP >= list_items) break;
       // snake order: even rounds ascend, odd rounds descend, so every CTA
       // pairs a heavy item with a light one
@@ -729,8 +754,8 @@ void prefill_kernel(PrefillParams p) {
     __amdgpu_buffer_rsrc_t krs_n = krs, vrs_n = vrs;
     if constexpr (kPrefetch) {
       const int nr = round + 1;
-      if (p.persistent && ntiles > 0 && nr * NP < list_items) {
-        const int wn = nr * NP + ((nr & 1) ? (NP - 1 - cta) : cta);
+      if (p.persistent && ntiles > 0 && (qmode || nr * NP < list_items)) {
+        const int wn = qmode ? uniform((int)q_item[nr & 1]) : nr * NP + ((nr & 1) ? (NP - 1 - cta) : cta);
         if (wn < list_items && locate(wn, N)) {
           pf = true;
           const int nb = N.Sk > 0 ? ((N.Sk - 1) * N.KRS + D) * 2 : 0;
@@ -750,6 +775,7 @@ void prefill_kernel(PrefillParams p) {
 
     auto run = [&](auto lag_c) {
       constexpr int LAG = decltype(lag_c)::value;
+      unsigned q_tk = 0;  // (thread 0) ticket in flight across the final two phases
       f32x16 S[NST];   // S of the tile between its M and V steps
       u32x4 P[NST][2];  // P of the tile between its V and next M steps
 #pragma unroll
@@ -766,6 +792,11 @@ void prefill_kernel(PrefillParams p) {
         // K/V copies that the following group issues in the same phase
         constexpr bool LAST = decltype(last_c)::value;
         if constexpr (LAST && kPrefetch) {
+          // the ticket for the item after the next one: taken at the start
+          // of the first final phase (ahead of the Q loads, so that waiting
+          // for it does not wait for them), written to LDS at the end of the
+          // second, so the atomic's round trip overlaps both
+          if (qmode && g == nphase - 2 && tid == 0) q_tk = add_flag(qctr(), 1u);
           if (pf && g == nphase - 2) load_q(N);
         }
         // the leading group copies K(X) in its V phase 2X - 2 NBUF + 3, the
@@ -838,6 +869,9 @@ void prefill_kernel(PrefillParams p) {
           for (int st = 0; st < NST; ++st) stage_exp(S[st], P[st]);
         }
         if constexpr (KIND == 0 && kMfmaPrio > 0) __builtin_amdgcn_s_setprio(0);
+        if constexpr (LAST && kPrefetch) {
+          if (qmode && g == nphase - 1 && tid == 0) q_tick = q_tk;
+        }
         // each phase is its own scheduling region: nothing drifts across the
         // barrier that separates the two waves' roles; the tile copied in
         // this phase has landed in LDS before the barrier
@@ -901,6 +935,14 @@ void prefill_kernel(PrefillParams p) {
         if constexpr (VARLEN) p.lse[(long long)hq * p.total_q + q_lo + row] = lse;
         else p.lse[((long long)b * p.Hq + hq) * Sq + row] = lse;
       }
+    }
+  }
+  if (qmode && tid == 0) {
+    // every ticket of this workgroup has been taken and used; the last
+    // workgroup to finish leaves the counters at zero for the next launch
+    if (add_flag(p.queue + kXcds, 1u) == gridDim.x - 1) {
+      for (int x = 0; x < kXcds; ++x) st_flag(p.queue + x, 0u);
+      st_flag(p.queue + kXcds, 0u);
     }
   }
 }

@@ -81,11 +81,14 @@ typedef enum {
  * Sk * D * 2 <= INT_MAX, else FA_ERR_SHAPE.
  * When the shape has fewer work items than the GPU has CUs, the keys of each
  * item are split over several workgroups (fa_fwd_plan reports split_tiles);
- * their partial results meet in a workspace that the library allocates once
- * per (device, stream) on the first such call, 34.6 MB held until the process
- * ends, so that first call is not capturable in a HIP graph.  Calls on one
- * stream reuse it in order; a graph captured with a split launch keeps using
- * the workspace of the stream it was captured on.
+ * their partial results meet in a workspace.  With at least as many items as
+ * CUs, the persistent workgroups take items from a work queue whose counters
+ * live in the same workspace.  The library allocates it once per (device,
+ * stream) on the first such call, 34.6 MB held until the process ends, so
+ * that first call is not capturable in a HIP graph.  Every launch leaves its
+ * counters at zero; calls on one stream reuse the workspace in order; a graph
+ * captured with such a launch keeps using the workspace of the stream it was
+ * captured on.
  */
 fa_status_t fa_fwd(const void* q, const void* k, const void* v, void* o,
                    int B, int Hq, int Hkv, int Sq, int Sk, int D,
@@ -159,6 +162,12 @@ typedef struct {
                            in the launch; chosen for non-persistent launches
                            whose longest item can be cut to at most
                            tiles - 2 tiles per part within one workgroup per CU */
+  int queue;            /* 1 = persistent launch whose workgroups take the items
+                           after their first from a work queue (an atomic
+                           ticket counter in the library's per-stream
+                           workspace), so the list is dealt to whichever
+                           workgroup is free; 0 = static round-robin.  Chosen
+                           for every persistent launch */
 } fa_fwd_plan_t;
 
 fa_status_t fa_fwd_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,
@@ -167,17 +176,17 @@ fa_status_t fa_fwd_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causa
 /*
  * fa_fwd_planned -- fa_fwd (and fa_fwd_lse when lse is not NULL) with the
  * launch schedule chosen by the caller: `plan` holds the choices in its
- * persistent, hkv_major, xcd_map (each 0 or 1) and split_tiles (>= 0) fields;
- * the other fields are ignored.  Without a split the schedule only decides
+ * persistent, hkv_major, xcd_map, queue (each 0 or 1) and split_tiles (>= 0)
+ * fields; the other fields are ignored.  Without a split the schedule only decides
  * which workgroup computes which work item and in what order, so every such
  * choice gives bitwise the same result.  A split (split_tiles > 0) sums each
  * item in parts and merges them: the result then differs from the unsplit one
  * by rounding only, and is the same bits call after call for one split_tiles.
  * It exists to compare schedules.  Choices that do not fit the sizes -- a
  * field out of range, xcd_map without a persistent grid of one workgroup per
- * CU (256) and B * Hkv a multiple of 8, a split together with persistent,
- * hkv_major or xcd_map, or a split of more than 256 parts -- give
- * FA_ERR_SHAPE.  Other arguments and errors as fa_fwd / fa_fwd_lse.
+ * CU (256) and B * Hkv a multiple of 8, queue without a persistent grid, a
+ * split together with persistent, hkv_major, xcd_map or queue, or a split of
+ * more than 256 parts -- give FA_ERR_SHAPE.  Other arguments and errors as fa_fwd / fa_fwd_lse.
  */
 fa_status_t fa_fwd_planned(const void* q, const void* k, const void* v, void* o, float* lse,
                            int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,

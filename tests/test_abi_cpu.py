@@ -55,7 +55,8 @@ def test_fwd_planned_checks_the_schedule_before_any_hip_call():
     # negative, and at most 256 parts (4096 keys / 128 per tile / 1 per part
     # x 16 blocks x 32 heads is far more)
     for fields in (dict(split_tiles=-1), dict(split_tiles=4, persistent=1),
-                   dict(split_tiles=4, hkv_major=1), dict(split_tiles=1)):
+                   dict(split_tiles=4, hkv_major=1), dict(split_tiles=1), dict(queue=2),
+                   dict(queue=1), dict(split_tiles=40, queue=1)):
         bad = _lib.FwdPlan()
         for key, value in fields.items():
             setattr(bad, key, value)
@@ -329,6 +330,7 @@ def test_work_items_and_orders():
     for c in FACTS["persistent_auto"]["cases"]:
         p = fa.fwd_plan(c["B"], c["Hq"], c["Hq"], c["Sq"], c["Sq"], 128, True)
         assert p["persistent"] == int(c["persistent"]), c
+        assert p["queue"] == int(c["persistent"])  # the work queue for persistent grids
         if c["persistent"]:
             assert p["grid"] == 256 and p["split_tiles"] == 0
         else:  # one workgroup per item, or per part of an item when keys are split

@@ -305,9 +305,12 @@ def test_persistent_and_grid_launches_agree_bitwise():
     assert fa.fwd_plan(B, Hq, Hkv, S, S, 128, True)["xcd_map"] == 1
     q, k, v = shape_inputs(B, Hq, Hkv, S, S, 128, dtype, seed=106)
     tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
-    outs = [run_fwd(q, k, v, True, 0.088, dtype)]  # the automatic plan
-    for pers, hkv, xcd in ((0, 0, 0), (0, 1, 0), (1, 0, 0), (1, 1, 0), (1, 0, 1), (1, 1, 1)):
-        sched = dict(persistent=pers, hkv_major=hkv, xcd_map=xcd)
+    outs = [run_fwd(q, k, v, True, 0.088, dtype)]  # the automatic plan (work queue)
+    assert fa.fwd_plan(B, Hq, Hkv, S, S, 128, True)["queue"] == 1
+    for pers, hkv, xcd, queue in ((0, 0, 0, 0), (0, 1, 0, 0), (1, 0, 0, 0), (1, 1, 0, 0),
+                                  (1, 0, 1, 0), (1, 1, 1, 0), (1, 0, 0, 1), (1, 1, 0, 1),
+                                  (1, 1, 1, 1)):
+        sched = dict(persistent=pers, hkv_major=hkv, xcd_map=xcd, queue=queue)
         outs.append(bits_of(fa.fwd(tq, tk, tv, causal=True, scale=0.088, schedule=sched)))
     # the key-split launch with parts of up to 8 tiles: every item here has at
     # most 1024 / 128 = 8 tiles, so each part is a whole item -- the split
@@ -387,6 +390,28 @@ def test_key_split_workspace_reused_across_shapes():
     assert np.array_equal(runs[0], runs[2])
 
 
+def test_work_queue_counters_reset_between_launches():
+    # persistent launches that deal items from the work queue, of different
+    # shapes and list splits in a row on one stream: each leaves its counters
+    # at zero, so repeating the first shape gives the same bits, and every
+    # item is computed exactly once (against the static schedule)
+    fa = _fa()
+    dtype = "bf16"
+    shapes = [(2, 32, 4, 1024, 1024, True), (1, 96, 8, 600, 900, True), (2, 32, 4, 1024, 1024, True),
+              (4, 32, 8, 512, 512, False)]
+    runs = []
+    for i, (B, Hq, Hkv, Sq, Sk, causal) in enumerate(shapes):
+        assert fa.fwd_plan(B, Hq, Hkv, Sq, Sk, 128, causal)["queue"] == 1
+        q, k, v = shape_inputs(B, Hq, Hkv, Sq, Sk, 128, dtype, seed=470 + 10 * (i % 2))
+        tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+        got = bits_of(fa.fwd(tq, tk, tv, causal=causal, scale=0.09))
+        static = bits_of(fa.fwd(tq, tk, tv, causal=causal, scale=0.09,
+                                schedule=dict(persistent=1, hkv_major=0, xcd_map=0, queue=0)))
+        assert np.array_equal(got, static), shapes[i]
+        runs.append(got)
+    assert np.array_equal(runs[0], runs[2])
+
+
 def test_planned_rejects_schedules_that_do_not_fit():
     import torch
     fa = _fa()
@@ -397,3 +422,5 @@ def test_planned_rejects_schedules_that_do_not_fit():
         fa.fwd(q, k, k, schedule=dict(persistent=1, hkv_major=0, xcd_map=1))
     with pytest.raises(fa.FaError):
         fa.fwd(q, k, k, schedule=dict(persistent=2, hkv_major=0, xcd_map=0))
+    with pytest.raises(fa.FaError):  # a work queue needs a persistent grid
+        fa.fwd(q, k, k, schedule=dict(persistent=0, hkv_major=0, xcd_map=0, queue=1))
