@@ -431,7 +431,7 @@ def bench_configs(fa, torch):
                        "dtype": s.dtype, "causal": s.causal, "useful_flop": flop, "calls": n,
                        "schedule": {key: plan[key] for key in ("work_items", "grid", "persistent",
                                                                "hkv_major", "xcd_map",
-                                                               "split_tiles")}}
+                                                               "split_tiles", "queue")}}
         del keep
     B, Hq, Hkv, D = 1, 8, 2, 128
     scale = 1 / math.sqrt(D)

@@ -505,8 +505,9 @@ void prefill_kernel(PrefillParams p) {
   bool have_pf = false;  // this item's Q and tile 0 were loaded by the one before
   int ring = 0;
   // Work queue (persistent launches with the prefetch): a workgroup's first
-  // item is its own index in its list; each later item is list position
-  // NP + t for a ticket t taken from the list's counter.  The ticket for the
+  // two items are list positions cta and NP + cta (no atomic before the
+  // first item); each later item is list position 2 NP + t for a ticket t
+  // taken from the list's counter.  The ticket for the
   // item after next is taken in an item's final phase, so the next item is
   // known (and prefetched) a whole item ahead and the atomic's latency hides
   // behind the item's end.  Items are dealt in list order (heaviest first
@@ -524,9 +525,13 @@ void prefill_kernel(PrefillParams p) {
     if (qmode) {
       w = round == 0 ? cta : uniform((int)q_item[round & 1]);
       if (tid == 0) {
-        unsigned t = round == 0 ? kEmpty : q_tick;
-        if (t == kEmpty) t = add_flag(qctr(), 1u);
-        q_item[(round + 1) & 1] = NP + min(t, kNoTicket);
+        unsigned nxt = NP + cta;
+        if (round > 0) {
+          unsigned t = q_tick;
+          if (t == kEmpty) t = add_flag(qctr(), 1u);
+          nxt = 2 * NP + min(t, kNoTicket);
+        }
+        q_item[(round + 1) & 1] = nxt;
         q_tick = kEmpty;
       }
       __syncthreads();

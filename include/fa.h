@@ -81,9 +81,9 @@ typedef enum {
  * Sk * D * 2 <= INT_MAX, else FA_ERR_SHAPE.
  * When the shape has fewer work items than the GPU has CUs, the keys of each
  * item are split over several workgroups (fa_fwd_plan reports split_tiles);
- * their partial results meet in a workspace.  With at least as many items as
- * CUs, the persistent workgroups take items from a work queue whose counters
- * live in the same workspace.  The library allocates it once per (device,
+ * their partial results meet in a workspace.  With at least 12 items per CU,
+ * the persistent workgroups take items from a work queue whose counters live
+ * in the same workspace.  The library allocates it once per (device,
  * stream) on the first such call, 34.6 MB held until the process ends, so
  * that first call is not capturable in a HIP graph.  Every launch leaves its
  * counters at zero; calls on one stream reuse the workspace in order; a graph
@@ -167,7 +167,8 @@ typedef struct {
                            ticket counter in the library's per-stream
                            workspace), so the list is dealt to whichever
                            workgroup is free; 0 = static round-robin.  Chosen
-                           for every persistent launch */
+                           for persistent launches of 12 or more items per
+                           workgroup, with the query-block-major order */
 } fa_fwd_plan_t;
 
 fa_status_t fa_fwd_plan(int B, int Hq, int Hkv, int Sq, int Sk, int D, int causal,

@@ -317,12 +317,18 @@ def test_work_items_and_orders():
     w = FACTS["work_items"]
     assert fa.fwd_plan(w["B"], w["Hq"], w["Hkv"], w["Sq"], w["Sq"], 128, True)["work_items"] == \
         w["value"]
+    # the page's order rule holds for the static persistent schedule; plans
+    # with the work queue (12+ items per workgroup) deal a query-block-major
+    # list instead
     for c in FACTS["hkv_major_rule"]["cases"]:
         p = fa.fwd_plan(c["B"], c["Hq"], c["Hkv"], c["Sq"], c["Sq"], 128, True)
-        assert p["hkv_major"] == (c["order"] == "hkv_major"), c
+        if p["queue"]:
+            assert p["work_items"] >= 12 * 256 and p["hkv_major"] == 0 and p["xcd_map"] == 0, c
+        else:
+            assert p["hkv_major"] == (c["order"] == "hkv_major"), c
     # XCD dealing: on for query-block-major persistent launches when the
     # B * Hkv units split over the 8 XCDs
-    assert fa.fwd_plan(1, 128, 8, 8192, 8192, 128, True)["xcd_map"] == 0  # kv-head-major
+    assert fa.fwd_plan(1, 128, 8, 8192, 8192, 128, True)["xcd_map"] == 0  # work queue
     assert fa.fwd_plan(4, 32, 8, 4096, 4096, 128, True)["xcd_map"] == 1
     assert fa.fwd_plan(4, 32, 8, 1000, 3000, 128, True)["xcd_map"] == 1
     assert fa.fwd_plan(1, 32, 4, 4096, 4096, 128, True)["xcd_map"] == 0   # 4 units
@@ -330,7 +336,8 @@ def test_work_items_and_orders():
     for c in FACTS["persistent_auto"]["cases"]:
         p = fa.fwd_plan(c["B"], c["Hq"], c["Hq"], c["Sq"], c["Sq"], 128, True)
         assert p["persistent"] == int(c["persistent"]), c
-        assert p["queue"] == int(c["persistent"])  # the work queue for persistent grids
+        # the work queue for persistent grids of 12+ items per workgroup
+        assert p["queue"] == int(c["persistent"] and p["work_items"] >= 12 * 256)
         if c["persistent"]:
             assert p["grid"] == 256 and p["split_tiles"] == 0
         else:  # one workgroup per item, or per part of an item when keys are split

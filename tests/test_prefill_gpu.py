@@ -305,8 +305,7 @@ def test_persistent_and_grid_launches_agree_bitwise():
     assert fa.fwd_plan(B, Hq, Hkv, S, S, 128, True)["xcd_map"] == 1
     q, k, v = shape_inputs(B, Hq, Hkv, S, S, 128, dtype, seed=106)
     tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
-    outs = [run_fwd(q, k, v, True, 0.088, dtype)]  # the automatic plan (work queue)
-    assert fa.fwd_plan(B, Hq, Hkv, S, S, 128, True)["queue"] == 1
+    outs = [run_fwd(q, k, v, True, 0.088, dtype)]  # the automatic plan
     for pers, hkv, xcd, queue in ((0, 0, 0, 0), (0, 1, 0, 0), (1, 0, 0, 0), (1, 1, 0, 0),
                                   (1, 0, 1, 0), (1, 1, 1, 0), (1, 0, 0, 1), (1, 1, 0, 1),
                                   (1, 1, 1, 1)):
@@ -401,10 +400,11 @@ def test_work_queue_counters_reset_between_launches():
               (4, 32, 8, 512, 512, False)]
     runs = []
     for i, (B, Hq, Hkv, Sq, Sk, causal) in enumerate(shapes):
-        assert fa.fwd_plan(B, Hq, Hkv, Sq, Sk, 128, causal)["queue"] == 1
+        assert fa.fwd_plan(B, Hq, Hkv, Sq, Sk, 128, causal)["persistent"] == 1
         q, k, v = shape_inputs(B, Hq, Hkv, Sq, Sk, 128, dtype, seed=470 + 10 * (i % 2))
         tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
-        got = bits_of(fa.fwd(tq, tk, tv, causal=causal, scale=0.09))
+        got = bits_of(fa.fwd(tq, tk, tv, causal=causal, scale=0.09,
+                             schedule=dict(persistent=1, hkv_major=i % 2, xcd_map=0, queue=1)))
         static = bits_of(fa.fwd(tq, tk, tv, causal=causal, scale=0.09,
                                 schedule=dict(persistent=1, hkv_major=0, xcd_map=0, queue=0)))
         assert np.array_equal(got, static), shapes[i]
