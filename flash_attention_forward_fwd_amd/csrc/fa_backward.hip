@@ -42,11 +42,15 @@ constexpr int kPipe = FA_BWD_PIPE;
 #endif
 constexpr int kDqKeys = FA_BWD_DQ_KEYS;
 constexpr int kDqWaves = kDqKeys == 32 ? 2 : 1;
-// dK/dV kernel: query rows per step
-#ifndef FA_BWD_DKDV_ROWS
-#define FA_BWD_DKDV_ROWS 64
+// dK/dV kernel: waves per workgroup (two groups of 4 sharing the block's keys)
+// and keys per workgroup
+constexpr int kDkdvWaves = 8;
+constexpr int kDkdvKeys = 128;
+// dK/dV: operand pairs (both MFMA operands from LDS) read this many MFMAs ahead
+#ifndef FA_BWD_PAIR_PIPE
+#define FA_BWD_PAIR_PIPE 3
 #endif
-constexpr int kDkdvRows = FA_BWD_DKDV_ROWS;
+constexpr int kPairPipe = FA_BWD_PAIR_PIPE;
 
 // A ROWS x D tile in flight between global memory and LDS: each of the
 // workgroup's threads holds N of its 16-byte chunks in registers, so the next
@@ -282,51 +286,147 @@ void bwd_dq_kernel(BwdParams p) {
   }
 }
 
-// ---- dkdv: one workgroup per (batch, kv head, 128 keys) -------------------------
+// the two operands of one MFMA, both read from LDS
+struct OpPair {
+  u32x4 a, b;
+};
+
+// ---- dkdv: one workgroup of 8 waves per (batch, kv head, 128 keys) ---------------
+// Waves w and w + 4 own the same 32 keys (K and V rows of the block stay in
+// LDS, read as B operands) and take alternate 32-row query tiles of the
+// (query head of the group, row tile) list: the leading group (waves 0-3) the
+// even tiles, the following group the odd ones.  The two groups run the
+// forward's ping-pong one phase apart, so the wave pair of a SIMD alternates
+// MFMA and vector work:
+//   M(t): dV^T += dO^T P and dK^T += Q^T dS of the group's tile t - 1 (dO^T, Q^T
+//         by transposing reads, P and dS from registers in their register
+//         order), then S = Q K^T and dP = dO V^T of its tile t: 32 MFMAs a wave
+//   V(t): P = exp2(S c - LSE log2 e) masked, dS = P (dP - D), packed to the
+//         input type; and the copy of the group's tile t + 1 into its LDS ring
+//         slot (buffer loads straight to LDS: no registers, no LDS stores)
+// Tile t is read as rows in M(t) and transposed in M(t + 1), so two ring slots
+// per group suffice: tile t + 1 lands in the slot of tile t - 1, whose last
+// read was in the M(t) just before.  At the end the following group's fp32
+// partial sums go through LDS and the leading group adds them (in that fixed
+// order, so results are deterministic) and writes dK = scale dK^T^T, dV.
 template <int D, int DT, bool CAUSAL>
-__global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(kDkdvWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dkdv_kernel(BwdParams p) {
   using E = Elt<DT>;
-  constexpr int BM = kDkdvRows;          // query rows per step (32-row sub-tiles)
-  constexpr int NST = BM / 32;
+  constexpr int BM = 32;                 // query rows per tile
   constexpr int KSTEPS = D / 16, DTILES = D / 32;
-  constexpr int QST = D + kTrPad;        // Q and dO: row reads and transposed reads
-  __shared__ __attribute__((aligned(16))) uint16_t Qs[BM * QST];
-  __shared__ __attribute__((aligned(16))) uint16_t Gs[BM * QST];
-  __shared__ __attribute__((aligned(16))) float Ls[BM];
-  __shared__ __attribute__((aligned(16))) float Ds[BM];
+  constexpr int KST = D + kRowPad;       // K, V rows: 16-byte row reads only
+  constexpr int QST = D + kTrPad;        // Q, dO rows: row reads and transposed reads
+  constexpr int KV = kDkdvKeys * KST;    // elements of the block's K (or V)
+  constexpr int TILE = BM * QST;         // elements of one Q (or dO) tile
+  constexpr int KRC = KST / 8, QRC = QST / 8;       // 16-byte chunks per LDS row
+  constexpr int KNI = kDkdvKeys * KRC / 64;         // 1 KiB pieces of a K (or V) image
+  constexpr int QNI = BM * QRC / 64;                // 1 KiB pieces of a Q (or dO) tile
+  static_assert(kDkdvKeys * KRC % 64 == 0 && BM * QRC % 64 == 0, "images are whole KiB");
+  constexpr int NPW = (2 * QNI + 3) / 4;            // tile pieces per wave of a group
+  // LDS: K, V | Q tiles [group][slot] | dO tiles [group][slot] | LSE, D [group][slot][64]
+  constexpr int Q_OFF = 2 * KV, G_OFF = Q_OFF + 4 * TILE, LD_OFF = G_OFF + 4 * TILE;
+  constexpr int LDS_ELEMS = LD_OFF + 2 * 4 * 64 * 2;   // floats as pairs of elements
+  // the final reduction: 4 waves x 64 lanes x (dK and dV: D floats per lane)
+  static_assert(LDS_ELEMS * 2 >= (kDkdvWaves / 2) * 64 * D * 4, "the final reduction fits");
+  __shared__ __attribute__((aligned(16))) uint16_t lds[LDS_ELEMS];
+  uint16_t* const Ks = lds;
+  uint16_t* const Vs = lds + KV;
+  float* const LD = reinterpret_cast<float*>(lds + LD_OFF);
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
+  const int grp = wave >> 2, gw = wave & 3;
   const int li = lane & 31, lh = lane >> 5, ti = lane & 15;
-  const int nkb = (p.Sk + 127) / 128;
-  int blk = blockIdx.x;
-  const int kb = blk % nkb;
-  blk /= nkb;
-  const int hk = blk % p.Hkv;
-  const int b = blk / p.Hkv;
-  const int k0 = kb * 128, kw0 = k0 + wave * 32, key = kw0 + li;
+  // blocks key-block-major: the heaviest causal key blocks of every head first
+  const int nkb = (p.Sk + kDkdvKeys - 1) / kDkdvKeys;
+  const int units = p.B * p.Hkv;
+  const int kb = (int)blockIdx.x / units, unit = (int)blockIdx.x - kb * units;
+  const int hk = unit % p.Hkv, b = unit / p.Hkv;
+  const int k0 = kb * kDkdvKeys, kw0 = k0 + 32 * gw, key = kw0 + li;
   const int Sq = p.Sq, Sk = p.Sk, kv_off = Sk - Sq;
   const long long kvbase = ((long long)b * p.Hkv + hk) * Sk * D;
-
-  // K (sign-folded: the scores come out as q_sign * S, the sign of the scale
-  // applied once here instead of to every Q tile) and V rows as B operands:
-  // lane key li, d = 16 kk + 8 lh + e
-  u32x4 kr[KSTEPS], vr[KSTEPS];
-#pragma unroll
-  for (int kk = 0; kk < KSTEPS; ++kk) {
-    u32x4 x = {0u, 0u, 0u, 0u}, y = {0u, 0u, 0u, 0u};
-    if (key < Sk) {
-      x = gload16(static_cast<const uint16_t*>(p.k) + kvbase + (long long)key * D + 16 * kk + 8 * lh);
-      y = gload16(static_cast<const uint16_t*>(p.v) + kvbase + (long long)key * D + 16 * kk + 8 * lh);
-    }
-    if (p.q_sign < 0) x ^= 0x80008000u;
-    if (p.q_sign == 0) x = u32x4{0u, 0u, 0u, 0u};
-    kr[kk] = x;
-    vr[kk] = y;
-  }
   const float c = p.c_log2;
-  const int v_lane = (4 * lh + (ti >> 2)) * QST + 16 * ((lane >> 4) & 1) + 4 * (ti & 3);
+  (void)nkb;
+
+  // row tiles that see a key of this block: row + kv_off >= k0 when causal;
+  // the (query head g of the group, row tile) list, g outermost
+  const int r_first = CAUSAL ? (max(0, k0 - kv_off) / BM) * BM : 0;
+  const int nrt = r_first < Sq ? (Sq - r_first + BM - 1) / BM : 0;
+  const int total = p.gqa * nrt;
+  const int n_lead = (total + 1) / 2, n_mine = grp == 0 ? n_lead : total / 2;
+  auto tile_row0 = [&](int t) {  // first row of this group's tile t
+    const int it = 2 * t + grp;
+    return r_first + (it % nrt) * BM;
+  };
+  auto tile_head = [&](int t) { return hk * p.gqa + (2 * t + grp) / nrt; };
+
+  // ---- copies (buffer loads to LDS, 1 KiB pieces; lane j of a load writes
+  // bytes [16 j, 16 j + 16) of its piece).  Image chunk c is row c / RC,
+  // column c % RC; padding columns and rows past the range read zeros.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(static_cast<const void*>(static_cast<const uint16_t*>(p.k) + kvbase)),
+      (short)0, Sk * D * 2, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(static_cast<const void*>(static_cast<const uint16_t*>(p.v) + kvbase)),
+      (short)0, Sk * D * 2, kBufferFlags);
+  {
+    // the block's K and V images, all 8 waves
+    for (int u = wave; u < 2 * KNI; u += kDkdvWaves) {
+      const int pc = u < KNI ? u : u - KNI;
+      const int cidx = 64 * pc + lane;
+      const int rr = cidx / KRC, cc = cidx - rr * KRC;
+      const unsigned off = cc < D / 8 ? (unsigned)(((k0 + rr) * D + cc * 8) * 2) : kPastEnd;
+      lds_dma16(u < KNI ? krs : vrs, (u < KNI ? Ks : Vs) + pc * 512, off, 0);
+    }
+  }
+  // this wave's per-lane source offsets inside a tile: pieces gw, gw + 4, ...
+  // of the Q image (pieces < QNI) then the dO image
+  unsigned toff[NPW];
+#pragma unroll
+  for (int i = 0; i < NPW; ++i) {
+    const int pc = gw + 4 * i;
+    const int pp = pc < QNI ? pc : pc - QNI;
+    const int cidx = 64 * pp + lane;
+    const int rr = cidx / QRC, cc = cidx - rr * QRC;
+    toff[i] = cc < D / 8 ? (unsigned)((rr * D + cc * 8) * 2) : kPastEnd;
+  }
+  // copy this group's tile t into ring slot t % 2 (the group's 4 waves), with
+  // the rows' LSE and D (wave gw == 0, 64 rows from r0, those past Sq zero)
+  auto copy_tile = [&](int t) {
+    const int r0 = tile_row0(t), hq = tile_head(t), slot = t & 1;
+    const int valid = min(BM, Sq - r0);
+    const long long qoff = (((long long)b * p.Hq + hq) * Sq + r0) * D;
+    const __amdgpu_buffer_rsrc_t qrs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(static_cast<const void*>(static_cast<const uint16_t*>(p.q) + qoff)),
+        (short)0, valid * D * 2, kBufferFlags);
+    const __amdgpu_buffer_rsrc_t grs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<void*>(static_cast<const void*>(static_cast<const uint16_t*>(p.dout) + qoff)),
+        (short)0, valid * D * 2, kBufferFlags);
+    uint16_t* qd = lds + Q_OFF + (grp * 2 + slot) * TILE;
+    uint16_t* gd = lds + G_OFF + (grp * 2 + slot) * TILE;
+#pragma unroll
+    for (int i = 0; i < NPW; ++i) {
+      const int pc = gw + 4 * i;
+      if (pc < QNI) lds_dma16(qrs, qd + pc * 512, toff[i], 0);
+      else if (pc < 2 * QNI) lds_dma16(grs, gd + (pc - QNI) * 512, toff[i], 0);
+    }
+    if (gw == 0) {
+      const long long srow = ((long long)b * p.Hq + hq) * Sq + r0;
+      const __amdgpu_buffer_rsrc_t lrs = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<float*>(p.lse + srow), (short)0, valid * 4, kBufferFlags);
+      const __amdgpu_buffer_rsrc_t drs = __builtin_amdgcn_make_buffer_rsrc(
+          p.dsum + srow, (short)0, valid * 4, kBufferFlags);
+      float* l = LD + ((grp * 2 + slot) * 2) * 64;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(lrs, (__attribute__((address_space(3))) void*)l, 4,
+                                               lane * 4, 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(drs, (__attribute__((address_space(3))) void*)(l + 64),
+                                               4, lane * 4, 0, 0, 0);
+    }
+  };
+  if (n_mine > 0) copy_tile(0);
+  wait_vmem();
+  __syncthreads();
 
   f32x16 dk[DTILES], dv[DTILES];
 #pragma unroll
@@ -334,127 +434,166 @@ void bwd_dkdv_kernel(BwdParams p) {
     dk[dt] = f32x16{};
     dv[dt] = f32x16{};
   }
+  const int v_lane = (4 * lh + (ti >> 2)) * QST + 16 * ((lane >> 4) & 1) + 4 * (ti & 3);
+  // the wave's keys as B operands: key kw0 + li, d = 16 kk + 8 lh + e
+  const uint16_t* const kb_row = Ks + (32 * gw + li) * KST + 8 * lh;
+  const uint16_t* const vb_row = Vs + (32 * gw + li) * KST + 8 * lh;
+  // K is the B operand of S = q_sign * Q K^T: the sign of the scale goes on
+  // the scores (exact), Q and K stay as stored
+  const float cs = p.q_sign == 0 ? 0.f : (p.q_sign < 0 ? -c : c);
 
-  // rows that see a key of this block: row + kv_off >= k0 when causal.  The
-  // steps run over (query head g of the group, 32-row tile) pairs; step it + 1
-  // is loaded into registers while step it is used.
-  const int r_first = CAUSAL ? (max(0, k0 - kv_off) / BM) * BM : 0;
-  const int nrt = r_first < Sq ? (Sq - r_first + BM - 1) / BM : 0;
-  const int total = p.gqa * nrt;
-  TileRegs<D, BM> qt, gt;
-  float lnext = 0.f, dnext = 0.f;
-  auto fetch = [&](int it) {
-    const int g = it / nrt;
-    const int r0 = r_first + (it - g * nrt) * BM;
-    const int hq = hk * p.gqa + g;
-    const long long qbase = ((long long)b * p.Hq + hq) * Sq * D + (long long)r0 * D;
-    const long long sbase = ((long long)b * p.Hq + hq) * Sq;
-    const int valid = min(BM, Sq - r0);
-    fetch_tile(qt, static_cast<const uint16_t*>(p.q) + qbase, valid);
-    fetch_tile(gt, static_cast<const uint16_t*>(p.dout) + qbase, valid);
-    if (tid < BM) {
-      const int r = r0 + tid;
-      lnext = r < Sq ? p.lse[sbase + r] * kLog2e : 0.f;
-      dnext = r < Sq ? p.dsum[sbase + r] : 0.f;
+  // tile t of this group is needed by this wave when the wave has keys and
+  // (causal) some pair of the tile is admissible
+  auto needed = [&](int t) {
+    if (t < 0 || t >= n_mine || kw0 >= Sk) return false;
+    return !CAUSAL || kw0 <= tile_row0(t) + BM - 1 + kv_off;
+  };
+
+  f32x16 S, dP;         // the tile between its M and V steps
+  u32x4 pb[2], db[2];   // P and dS of the tile between its V and next M steps
+  S = f32x16{};
+  dP = f32x16{};
+  auto run = [&](auto lag_c) {
+    constexpr int LAG = decltype(lag_c)::value;
+    const int nphase = n_lead > 0 ? 2 * n_lead + 2 : 0;
+    // one phase of kind KIND (0: M step, 1: V step) of this group
+    auto phase = [&](int g, auto kind_c) {
+      constexpr int KIND = decltype(kind_c)::value;
+      const int step = g - LAG;
+      const int t = step >> 1;
+      bool do_load = false;
+      if (KIND == 0 && step >= 0) {
+        // ---- M(t)
+        const bool pv = needed(t - 1), qk = needed(t);
+        if (pv) {
+          const int sl = (t - 1) & 1;
+          const uint16_t* Gb = lds + G_OFF + (grp * 2 + sl) * TILE;
+          const uint16_t* Qb = lds + Q_OFF + (grp * 2 + sl) * TILE;
+          // MFMA j: (k-step kk, column tile dt), dV (j even) or dK
+          auto load = [&](auto jc) -> u32x4 {
+            constexpr int j = decltype(jc)::value, dt = (j / 2) % DTILES, kk = j / (2 * DTILES);
+            const uint16_t* src = ((j % 2) ? Qb : Gb) + v_lane + 16 * kk * QST + 32 * dt;
+            const u32x2 lo = lds_read_tr16(src), hi = lds_read_tr16(src + 8 * QST);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+          };
+          auto mfma = [&](auto jc, u32x4 a) {
+            constexpr int j = decltype(jc)::value, dt = (j / 2) % DTILES, kk = j / (2 * DTILES);
+            if constexpr (j % 2) dk[dt] = E::mfma(a, db[kk], dk[dt]);
+            else dv[dt] = E::mfma(a, pb[kk], dv[dt]);
+          };
+          m_pipeline<4 * DTILES, kPipe>(load, mfma);
+        }
+        if (qk) {
+          const int sl = t & 1;
+          const uint16_t* Qb = lds + Q_OFF + (grp * 2 + sl) * TILE + li * QST + 8 * lh;
+          const uint16_t* Gb = lds + G_OFF + (grp * 2 + sl) * TILE + li * QST + 8 * lh;
+          // S = Q K^T and dP = dO V^T, alternating; both operands from LDS,
+          // read together kPipe MFMAs ahead
+          auto load = [&](auto jc) -> OpPair {
+            constexpr int j = decltype(jc)::value, kk = j / 2;
+            return OpPair{lds_read16(((j % 2) ? Gb : Qb) + 16 * kk),
+                          lds_read16(((j % 2) ? vb_row : kb_row) + 16 * kk)};
+          };
+          auto mfma = [&](auto jc, const OpPair& o) {
+            constexpr int j = decltype(jc)::value, kk = j / 2;
+            if constexpr (j % 2) dP = E::mfma(o.a, o.b, kk == 0 ? f32x16{} : dP);
+            else S = E::mfma(o.a, o.b, kk == 0 ? f32x16{} : S);
+          };
+          m_pipeline<2 * KSTEPS, kPairPipe>(load, mfma);
+        }
+      } else if (KIND == 1 && step >= 0) {
+        // ---- V(t): the rows' LSE and D first (LDS reads before this phase's
+        // copy is issued), then the copy of tile t + 1, then the gradient math
+        const bool use = needed(t);
+        const int r0 = tile_row0(t), sl = t & 1;
+        const float* l = LD + ((grp * 2 + sl) * 2) * 64;
+        // the rows' LSE and D of the first half (registers 0-7) before this
+        // phase's copy is issued, the second half's after the first half's math
+        f32x4 lse4[2], d4[2];
+        auto read_ld = [&](int half) {
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            lse4[q] = *reinterpret_cast<const f32x4*>(l + 16 * half + 8 * q + 4 * lh);
+            d4[q] = *reinterpret_cast<const f32x4*>(l + 64 + 16 * half + 8 * q + 4 * lh);
+          }
+        };
+        if (use) read_ld(0);
+        if (t + 1 < n_mine) {
+          copy_tile(t + 1);
+          do_load = true;
+        }
+        if (use) {
+          // lane = key; register r is query row r0 + 8 (r/4) + 4 lh + r%4.  Every
+          // exp2 is evaluated and masked pairs are selected to 0 (no branch).
+          const bool full = r0 + BM <= Sq && kw0 + 32 <= Sk && (!CAUSAL || kw0 + 31 <= r0 + kv_off);
+          auto grad = [&](auto mask_c, auto half_c) {
+            constexpr bool MASK = decltype(mask_c)::value;
+            constexpr int H = decltype(half_c)::value;
+#pragma unroll
+            for (int r = 8 * H; r < 8 * H + 8; ++r) {
+              const int rowi = r0 + 8 * (r >> 2) + 4 * lh + (r & 3);
+              const bool ok = !MASK || (rowi < Sq && key < Sk && (!CAUSAL || key <= rowi + kv_off));
+              const float e =
+                  fast_exp2(__builtin_fmaf(S[r], cs, -lse4[(r >> 2) & 1][r & 3] * kLog2e));
+              const float pr = ok ? e : 0.f;
+              S[r] = pr;
+              dP[r] = pr * (dP[r] - d4[(r >> 2) & 1][r & 3]);
+            }
+            const int q = 8 * H;
+            pb[H] = u32x4{E::pack2(S[q + 0], S[q + 1]), E::pack2(S[q + 2], S[q + 3]),
+                          E::pack2(S[q + 4], S[q + 5]), E::pack2(S[q + 6], S[q + 7])};
+            db[H] = u32x4{E::pack2(dP[q + 0], dP[q + 1]), E::pack2(dP[q + 2], dP[q + 3]),
+                          E::pack2(dP[q + 4], dP[q + 5]), E::pack2(dP[q + 6], dP[q + 7])};
+          };
+          using H0 = std::integral_constant<int, 0>;
+          using H1 = std::integral_constant<int, 1>;
+          if (full) grad(std::false_type{}, H0{});
+          else grad(std::true_type{}, H0{});
+          __builtin_amdgcn_sched_barrier(0);
+          read_ld(1);
+          if (full) grad(std::false_type{}, H1{});
+          else grad(std::true_type{}, H1{});
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (do_load) wait_vmem();
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    // phase g runs step g - LAG: an M step when it is even, a V step when odd
+    using K0 = std::integral_constant<int, LAG>;
+    using K1 = std::integral_constant<int, 1 - LAG>;
+    for (int g = 0; g < nphase; g += 2) {
+      phase(g, K0{});
+      phase(g + 1, K1{});
     }
   };
-  if (total > 0) fetch(0);
-  for (int it = 0; it < total; ++it) {
-    {
-      const int r0 = r_first + (it % nrt) * BM;
-      __syncthreads();  // the previous tile is no longer read
-      store_tile<D, BM, QST>(Qs, qt);
-      store_tile<D, BM, QST>(Gs, gt);
-      if (tid < BM) {
-        Ls[tid] = lnext;
-        Ds[tid] = dnext;
-      }
-      __syncthreads();
-      if (it + 1 < total) fetch(it + 1);
-      if (kw0 >= Sk) continue;                            // no keys in this wave
-      if (CAUSAL && kw0 > r0 + BM - 1 + kv_off) continue;  // every pair masked
-      // S = Q K^T and dP = dO V^T, the two products' MFMAs alternating, each
-      // LDS operand read kPipe MFMAs ahead (one wave per SIMD: nothing else
-      // hides the LDS latency)
-      f32x16 S[NST], dP[NST];
-      {
-        auto load = [&](auto jc) -> u32x4 {
-          constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
-          const uint16_t* src = (j % 2) ? Gs : Qs;
-          return lds_read16(src + (32 * st + li) * QST + 16 * kk + 8 * lh);
-        };
-        auto mfma = [&](auto jc, u32x4 a) {
-          constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
-          if constexpr (j % 2) dP[st] = E::mfma(a, vr[kk], kk == 0 ? f32x16{} : dP[st]);
-          else S[st] = E::mfma(a, kr[kk], kk == 0 ? f32x16{} : S[st]);
-        };
-        m_pipeline<2 * NST * KSTEPS, kPipe>(load, mfma);
-      }
-      // lane = key; register r of sub-tile st is query row r0 + 32 st + 8 (r/4) + 4 lh + r%4
-      u32x4 pb[NST][2], db[NST][2];
-      // every pair of this step is admissible for this wave when all its
-      // rows and keys exist and (causal) its last key is at or below its
-      // first row's diagonal: the mask is then left out
-      const bool full = r0 + BM <= Sq && kw0 + 32 <= Sk && (!CAUSAL || kw0 + 31 <= r0 + kv_off);
-      auto grad = [&](auto mask_c) {
-        constexpr bool MASK = decltype(mask_c)::value;
-#pragma unroll
-        for (int st = 0; st < NST; ++st) {
-          // the rows' LSE and D, four consecutive rows per 16-byte read, read
-          // before any is used; every exp2 is evaluated and masked pairs are
-          // then selected to 0, so the loop has no branch
-          f32x4 lse4[4], d4[4];
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            lse4[q] = *reinterpret_cast<const f32x4*>(Ls + 32 * st + 8 * q + 4 * lh);
-            d4[q] = *reinterpret_cast<const f32x4*>(Ds + 32 * st + 8 * q + 4 * lh);
-          }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int rr = 32 * st + 8 * (r >> 2) + 4 * lh + (r & 3);
-            const int rowi = r0 + rr;
-            const bool ok = !MASK || (rowi < Sq && key < Sk && (!CAUSAL || key <= rowi + kv_off));
-            const float e = fast_exp2(__builtin_fmaf(S[st][r], c, -lse4[r >> 2][r & 3]));
-            const float pr = ok ? e : 0.f;
-            S[st][r] = pr;
-            dP[st][r] = pr * (dP[st][r] - d4[r >> 2][r & 3]);
-          }
-#pragma unroll
-          for (int kk = 0; kk < 2; ++kk) {
-            const int q = 8 * kk;
-            pb[st][kk] = u32x4{E::pack2(S[st][q + 0], S[st][q + 1]), E::pack2(S[st][q + 2], S[st][q + 3]),
-                               E::pack2(S[st][q + 4], S[st][q + 5]), E::pack2(S[st][q + 6], S[st][q + 7])};
-            db[st][kk] = u32x4{E::pack2(dP[st][q + 0], dP[st][q + 1]), E::pack2(dP[st][q + 2], dP[st][q + 3]),
-                               E::pack2(dP[st][q + 4], dP[st][q + 5]), E::pack2(dP[st][q + 6], dP[st][q + 7])};
-          }
-        }
-      };
-      if (full) grad(std::false_type{});
-      else grad(std::true_type{});
-      // dV^T += dO^T P and dK^T += Q^T dS: dO^T, Q^T by transposing reads,
-      // rows in the register order of P and dS
-      {
-        // MFMA j: (sub-tile st, k-step kk, column tile dt), dV (j even) or dK
-        auto load = [&](auto jc) -> u32x4 {
-          constexpr int j = decltype(jc)::value, dt = (j / 2) % DTILES;
-          constexpr int kk = (j / (2 * DTILES)) % 2, st = j / (4 * DTILES);
-          const uint16_t* src = ((j % 2) ? Qs : Gs) + v_lane + (32 * st + 16 * kk) * QST + 32 * dt;
-          const u32x2 lo = lds_read_tr16(src), hi = lds_read_tr16(src + 8 * QST);
-          return u32x4{lo[0], lo[1], hi[0], hi[1]};
-        };
-        auto mfma = [&](auto jc, u32x4 a) {
-          constexpr int j = decltype(jc)::value, dt = (j / 2) % DTILES;
-          constexpr int kk = (j / (2 * DTILES)) % 2, st = j / (4 * DTILES);
-          if constexpr (j % 2) dk[dt] = E::mfma(a, db[st][kk], dk[dt]);
-          else dv[dt] = E::mfma(a, pb[st][kk], dv[dt]);
-        };
-        m_pipeline<4 * NST * DTILES, kPipe>(load, mfma);
-      }
-    }
-  }
+  if (grp == 0) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
 
-  // dK = scale * (dS^T Q), dV = P^T dO: lane key li, d = 32 dt + 8 (r/4) + 4 lh + r%4
-  if (key < Sk) {
+  // ---- the two groups' partial sums: the following group's through LDS
+  // (the ring is no longer read), added by the leading group in that order
+  float* red = reinterpret_cast<float*>(lds);
+  if (grp == 1) {
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        red[((gw * 2 * DTILES + dt) * 16 + r) * 64 + lane] = dk[dt][r];
+        red[((gw * 2 * DTILES + DTILES + dt) * 16 + r) * 64 + lane] = dv[dt][r];
+      }
+  }
+  __syncthreads();
+  if (grp == 0 && key < Sk) {
+#pragma unroll
+    for (int dt = 0; dt < DTILES; ++dt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        dk[dt][r] += red[((gw * 2 * DTILES + dt) * 16 + r) * 64 + lane];
+        dv[dt][r] += red[((gw * 2 * DTILES + DTILES + dt) * 16 + r) * 64 + lane];
+      }
+    // dK = scale * (dS^T Q) with the signed scale, dV = P^T dO: lane key li,
+    // d = 32 dt + 8 (r/4) + 4 lh + r%4
     uint16_t* krow = static_cast<uint16_t*>(p.dk) + kvbase + (long long)key * D + 4 * lh;
     uint16_t* vrow = static_cast<uint16_t*>(p.dv) + kvbase + (long long)key * D + 4 * lh;
     const float sc = p.scale;
@@ -487,9 +626,10 @@ hipError_t launch_bwd_c(const BwdParams& p, hipStream_t stream) {
     const hipError_t e2 = hipGetLastError();
     if (e2 != hipSuccess) return e2;
   }
-  if (nkb > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, CAUSAL>), dim3(p.B * p.Hkv * nkb),
-                       dim3(kBwdWaves * 64), 0, stream, p);
+  const int nkb2 = (p.Sk + kDkdvKeys - 1) / kDkdvKeys;
+  if (nkb2 > 0 && p.B * p.Hkv > 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, CAUSAL>), dim3(p.B * p.Hkv * nkb2),
+                       dim3(kDkdvWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 

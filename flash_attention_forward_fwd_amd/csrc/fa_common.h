@@ -175,10 +175,10 @@ constexpr float kLn2 = 0.693147180559945309417232121458f;
 // A run of N MFMAs as an explicit software pipeline: the LDS operand of
 // MFMA j is read LA MFMAs before it, and a scheduling fence after
 // every (MFMA j, read j + LA) pair keeps that distance from being collapsed
-// by the compiler's own scheduling.  load(j) returns MFMA j's operand,
-// mfma(j, a) issues MFMA j.
-template <int J, int N, int LA, class Load, class Mfma>
-__device__ __forceinline__ void m_pipe(Load& load, Mfma& mfma, u32x4 (&buf)[LA]) {
+// by the compiler's own scheduling.  load(j) returns MFMA j's operand (or
+// operands: any value type), mfma(j, a) issues MFMA j.
+template <int J, int N, int LA, class Load, class Mfma, class T>
+__device__ __forceinline__ void m_pipe(Load& load, Mfma& mfma, T (&buf)[LA]) {
   if constexpr (J < N) {
     mfma(std::integral_constant<int, J>{}, buf[J % LA]);
     if constexpr (J + LA < N) buf[J % LA] = load(std::integral_constant<int, J + LA>{});
@@ -186,8 +186,8 @@ __device__ __forceinline__ void m_pipe(Load& load, Mfma& mfma, u32x4 (&buf)[LA])
     m_pipe<J + 1, N, LA>(load, mfma, buf);
   }
 }
-template <int J, int N, int LA, class Load>
-__device__ __forceinline__ void m_prime(Load& load, u32x4 (&buf)[LA]) {
+template <int J, int N, int LA, class Load, class T>
+__device__ __forceinline__ void m_prime(Load& load, T (&buf)[LA]) {
   if constexpr (J < N && J < LA) {
     buf[J] = load(std::integral_constant<int, J>{});
     m_prime<J + 1, N, LA>(load, buf);
@@ -195,7 +195,8 @@ __device__ __forceinline__ void m_prime(Load& load, u32x4 (&buf)[LA]) {
 }
 template <int N, int LA, class Load, class Mfma>
 __device__ __forceinline__ void m_pipeline(Load& load, Mfma& mfma) {
-  u32x4 buf[LA];
+  using T = decltype(load(std::integral_constant<int, 0>{}));
+  T buf[LA];
   m_prime<0, N, LA>(load, buf);
   __builtin_amdgcn_sched_barrier(0);
   m_pipe<0, N, LA>(load, mfma, buf);
