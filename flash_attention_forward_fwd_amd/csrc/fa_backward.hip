@@ -5,22 +5,21 @@
 // recomputed tile by tile, no score matrix is stored):
 //
 //   pre   D_i = sum_d dO[i,d] O[i,d]                                 (fp32)
-//   dq    per 128 query rows, 32 keys a step (few enough registers for two
-//         waves per SIMD): S^T = K Q^T, dP^T = V dO^T,
-//         P = exp2(S c - LSE_i log2 e), dS = P (dP - D_i),
-//         dQ^T += K^T dS^T                       (Q and dO stay in registers)
-//   dkdv  per 128 keys, 64 query rows a step: S = Q K^T, dP = dO V^T, P and dS as above,
-//         dV^T += dO^T P, dK^T += Q^T dS   (K and V stay in registers; the
-//         query heads of a GQA group add into their kv head in the loop, so
-//         no atomics are needed anywhere)
+//   dq    per 256 query rows (8 waves, Q and dO in registers), 32-key K/V
+//         tiles: S^T = K Q^T, dP^T = V dO^T, P = exp2(S c - LSE_i log2 e),
+//         dS = P (dP - D_i), dQ^T += K^T dS^T
+//   dkdv  per 128 keys (8 waves, K and V in LDS), 32-row Q/dO tiles:
+//         S = Q K^T, dP = dO V^T, P and dS as above, dV^T += dO^T P,
+//         dK^T += Q^T dS; the query heads of a GQA group add into their kv
+//         head inside the loop, so no atomics are needed anywhere
 //
-// Every product runs on the 32x32x16 matrix core with the operand layouts of
-// the forward kernel: a wave owns 32 rows (dq) or 32 keys (dkdv), the operand
-// that varies along the loop is read from LDS, transposed operands come from
-// the gfx950 transposing LDS read, and P / dS feed the next product straight
-// from the accumulator registers in their register order.  Tiles are staged
-// global -> registers -> LDS with one barrier on each side; this version
-// favours simplicity over overlap.
+// Both main kernels follow the forward: two groups of 4 waves, one wave of
+// each per SIMD, run one phase apart (MFMA phase against vector phase), with
+// a workgroup barrier per phase; tiles are copied by buffer loads straight to
+// LDS in the vector phases; every product runs on the 32x32x16 matrix core
+// with the forward's operand layouts (transposed operands from the gfx950
+// transposing LDS read, P and dS fed from the accumulator registers in their
+// register order).
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -28,7 +27,6 @@ namespace fa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kBwdWaves = 4;        // waves per workgroup, 32 rows or keys each
 constexpr int kRowPad = 8;          // pad of tiles read by 16-byte row reads only
 constexpr int kTrPad = 32;          // pad of tiles that are also read transposed
 // MFMAs an LDS operand read runs ahead of its use
@@ -36,12 +34,13 @@ constexpr int kTrPad = 32;          // pad of tiles that are also read transpose
 #define FA_BWD_PIPE 4
 #endif
 constexpr int kPipe = FA_BWD_PIPE;
-// dQ kernel: keys per K/V tile, and the waves per SIMD its registers must allow
+// dQ kernel: keys per K/V tile (32; 64 needs more registers than two waves
+// per SIMD allow at D = 128), waves per workgroup (two groups)
 #ifndef FA_BWD_DQ_KEYS
 #define FA_BWD_DQ_KEYS 32
 #endif
 constexpr int kDqKeys = FA_BWD_DQ_KEYS;
-constexpr int kDqWaves = kDqKeys == 32 ? 2 : 1;
+constexpr int kDqWaves = 8;
 // dK/dV kernel: waves per workgroup (two groups of 4 sharing the block's keys)
 // and keys per workgroup
 constexpr int kDkdvWaves = 8;
@@ -51,53 +50,6 @@ constexpr int kDkdvKeys = 128;
 #define FA_BWD_PAIR_PIPE 3
 #endif
 constexpr int kPairPipe = FA_BWD_PAIR_PIPE;
-
-// A ROWS x D tile in flight between global memory and LDS: each of the
-// workgroup's threads holds N of its 16-byte chunks in registers, so the next
-// tile's loads can be issued before the current tile is used.
-template <int D, int ROWS>
-struct TileRegs {
-  static constexpr int CH = D / 8;                          // chunks per row
-  static constexpr int N = ROWS * CH / (kBwdWaves * 64);    // chunks per thread
-  static_assert(ROWS * CH % (kBwdWaves * 64) == 0, "whole chunks per thread");
-  u32x4 x[N];
-};
-
-// Load `valid` rows (row stride D elements in global memory) of a tile; rows
-// past `valid` are zero.  The tile is a buffer range that ends after its last
-// valid row, so those rows read zeros without a branch per load.  `src` and
-// `valid` are the same for every lane.
-template <int D, int ROWS>
-__device__ __forceinline__ void fetch_tile(TileRegs<D, ROWS>& t, const uint16_t* src, int valid) {
-  using T = TileRegs<D, ROWS>;
-  // read from the first lane so that the range is built in scalar registers
-  const uintptr_t a = reinterpret_cast<uintptr_t>(src);
-  const uintptr_t lo = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)a);
-  const uintptr_t hi = (unsigned)__builtin_amdgcn_readfirstlane((int)(unsigned)(a >> 32));
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
-      reinterpret_cast<uint16_t*>((hi << 32) | lo), (short)0, max(uniform(valid), 0) * D * 2,
-      kBufferFlags);
-#pragma unroll
-  for (int i = 0; i < T::N; ++i) {
-    const int c = (int)threadIdx.x + i * kBwdWaves * 64;
-    const int r = c / T::CH, cc = c - r * T::CH;
-    t.x[i] = __builtin_bit_cast(u32x4,
-                                __builtin_amdgcn_raw_buffer_load_b128(rs, (r * D + cc * 8) * 2, 0, 0));
-  }
-}
-
-// Write a fetched tile to LDS rows of LST elements.
-template <int D, int ROWS, int LST>
-__device__ __forceinline__ void store_tile(uint16_t* lds, const TileRegs<D, ROWS>& t) {
-  using T = TileRegs<D, ROWS>;
-#pragma unroll
-  for (int i = 0; i < T::N; ++i) {
-    const int c = (int)threadIdx.x + i * kBwdWaves * 64;
-    const int r = c / T::CH, cc = c - r * T::CH;
-    lds_write16(lds + r * LST + cc * 8, t.x[i]);
-  }
-}
-
 
 // ---- pre: D_i = rowsum(dO * O), 8 threads per row ------------------------------
 template <int D, int DT>
@@ -127,35 +79,53 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
   if (row < rows && part == 0) p.dsum[row] = acc;
 }
 
-// ---- dq: one workgroup per (batch, query head, 128 query rows) ------------------
+// ---- dq: one workgroup of 8 waves per (batch, query head, 256 query rows) ---------
+// The forward's structure: each wave owns 32 rows (Q and dO resident in
+// registers as B operands), the two wave groups walk the same 32-key K/V
+// tiles one phase apart:
+//   M(t): dQ^T += K^T dS^T of tile t - 1 (K^T by transposing reads), then
+//         S^T = K Q^T and dP^T = V dO^T of tile t: 24 MFMAs a wave
+//   V(t): P = exp2(S c - LSE log2 e) masked, dS = P (dP - D), packed, and
+//         the copies of the ring below
+// K(t) is read as rows in phases 2t, 2t + 1 and transposed in 2t + 2, 2t + 3;
+// V(t) as rows in 2t, 2t + 1.  So K has a ring of three slots and V of two:
+// the leading group copies K(X) in phase 2X - 1 into the slot of K(X - 3),
+// last read in 2X - 3; the following group copies V(X) in phase 2X - 2 into
+// the slot of V(X - 2), last read in 2X - 3; each copy lands before the
+// barrier ahead of its first read.
 template <int D, int DT, bool CAUSAL>
-__global__ __launch_bounds__(kBwdWaves * 64) __attribute__((amdgpu_waves_per_eu(kDqWaves, 2)))
+__global__ __launch_bounds__(kDqWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void bwd_dq_kernel(BwdParams p) {
   using E = Elt<DT>;
-  constexpr int BN = kDqKeys;            // keys per tile (32-key sub-tiles)
+  constexpr int BM = 32 * kDqWaves;      // query rows per workgroup
+  constexpr int BN = kDqKeys;            // keys per K/V tile (32-key sub-tiles)
   constexpr int NST = BN / 32;
   constexpr int KSTEPS = D / 16, DTILES = D / 32;
   constexpr int KST = D + kTrPad;        // K: row reads (S) and transposed reads (dQ)
   constexpr int VST = D + kRowPad;       // V: row reads (dP)
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[BN * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t Vs[BN * VST];
+  constexpr int KRC = KST / 8, VRC = VST / 8;
+  // 1 KiB pieces per tile image, rounded up: the chunks past the tile's BN
+  // rows land in the slot's tail and are never read
+  constexpr int KNI = (BN * KRC + 63) / 64, VNI = (BN * VRC + 63) / 64;
+  constexpr int KT = KNI * 512, VT = VNI * 512;             // slot sizes in elements
+  constexpr int KPW = (KNI + 3) / 4, VPW = (VNI + 3) / 4;   // pieces per wave of a group
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[3 * KT];
+  __shared__ __attribute__((aligned(16))) uint16_t Vs[2 * VT];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = uniform(tid >> 6);
   const int li = lane & 31, lh = lane >> 5, ti = lane & 15;
-  const int nqb = (p.Sq + 127) / 128;
-  int blk = blockIdx.x;
-  const int qb = blk % nqb;
-  blk /= nqb;
-  const int hq = blk % p.Hq;
-  const int b = blk / p.Hq;
+  const int grp = wave >> 2, gw = wave & 3;
+  // items heaviest first: query block level descending, then batch and head
+  const int nqb = (p.Sq + BM - 1) / BM;
+  const int per_lvl = p.B * p.Hq;
+  const int lvl = (int)blockIdx.x / per_lvl, rr0 = (int)blockIdx.x - lvl * per_lvl;
+  const int qb = nqb - 1 - lvl, b = rr0 / p.Hq, hq = rr0 - b * p.Hq;
   const int hk = hq / p.gqa;
-  const int q0 = qb * 128, rw0 = q0 + wave * 32, row = rw0 + li;
+  const int q0 = qb * BM, rw0 = q0 + wave * 32, row = rw0 + li;
   const int Sq = p.Sq, Sk = p.Sk, kv_off = Sk - Sq;
   const long long qbase = ((long long)b * p.Hq + hq) * Sq * D;   // q, dO, dQ
   const long long kvbase = ((long long)b * p.Hkv + hk) * Sk * D;
-  const uint16_t* kg = static_cast<const uint16_t*>(p.k) + kvbase;
-  const uint16_t* vg = static_cast<const uint16_t*>(p.v) + kvbase;
 
   // Q (sign-folded) and dO rows as B operands: lane row li, d = 16 kk + 8 lh + e
   u32x4 qr[KSTEPS], gr[KSTEPS];
@@ -177,99 +147,163 @@ void bwd_dq_kernel(BwdParams p) {
   const float dr = row < Sq ? p.dsum[srow] : 0.f;
   const float c = p.c_log2;
 
+  // keys [0, kv_end) are streamed for the workgroup; this wave needs [0, wave_end)
   int kv_end = Sk, wave_end = Sk;
   if (CAUSAL) {
-    kv_end = min(max(min(Sq, q0 + 128) + kv_off, 0), Sk);
+    kv_end = min(max(min(Sq, q0 + BM) + kv_off, 0), Sk);
     wave_end = min(max(min(Sq, rw0 + 32) + kv_off, 0), Sk);
   }
   if (rw0 >= Sq) wave_end = 0;
   const int ntiles = (kv_end + BN - 1) / BN;
   const int v_lane = (4 * lh + (ti >> 2)) * KST + 16 * ((lane >> 4) & 1) + 4 * (ti & 3);
 
+  // tile copies: the leading group copies K images, the following group V
+  const int kv_bytes = Sk > 0 ? Sk * D * 2 : 0;
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(static_cast<const void*>(static_cast<const uint16_t*>(p.k) + kvbase)),
+      (short)0, kv_bytes, kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<void*>(static_cast<const void*>(static_cast<const uint16_t*>(p.v) + kvbase)),
+      (short)0, kv_bytes, kBufferFlags);
+  const bool lead = grp == 0;
+  constexpr int NPW = KPW > VPW ? KPW : VPW;
+  unsigned offs[NPW];
+#pragma unroll
+  for (int u = 0; u < NPW; ++u) {
+    const int rc = lead ? KRC : VRC;
+    const int cidx = 64 * (gw + 4 * u) + lane;
+    const int rr = cidx / rc, cc = cidx - rr * rc;
+    offs[u] = cc < D / 8 ? (unsigned)((rr * D + cc * 8) * 2) : kPastEnd;
+  }
+  auto copy = [&](int X) {
+    if (lead) {
+      uint16_t* dst = Ks + (X % 3) * KT;
+#pragma unroll
+      for (int u = 0; u < KPW; ++u)
+        if (gw + 4 * u < KNI) lds_dma16(krs, dst + (gw + 4 * u) * 512, offs[u], X * BN * D * 2);
+    } else {
+      uint16_t* dst = Vs + (X % 2) * VT;
+#pragma unroll
+      for (int u = 0; u < VPW; ++u)
+        if (gw + 4 * u < VNI) lds_dma16(vrs, dst + (gw + 4 * u) * 512, offs[u], X * BN * D * 2);
+    }
+  };
+  if (ntiles > 0) copy(0);
+  wait_vmem();
+  __syncthreads();
+
   f32x16 dq[DTILES];
 #pragma unroll
   for (int dt = 0; dt < DTILES; ++dt) dq[dt] = f32x16{};
 
-  // tile t + 1 is loaded into registers while tile t is used
-  TileRegs<D, BN> kt, vt;
-  if (ntiles > 0) {
-    fetch_tile(kt, kg, min(BN, Sk));
-    fetch_tile(vt, vg, min(BN, Sk));
-  }
-  for (int t = 0; t < ntiles; ++t) {
-    __syncthreads();  // the previous tile is no longer read
-    store_tile<D, BN, KST>(Ks, kt);
-    store_tile<D, BN, VST>(Vs, vt);
-    __syncthreads();
-    if (t + 1 < ntiles) {
-      const int valid = min(BN, Sk - (t + 1) * BN);
-      fetch_tile(kt, kg + (long long)(t + 1) * BN * D, valid);
-      fetch_tile(vt, vg + (long long)(t + 1) * BN * D, valid);
-    }
-    if (t * BN >= wave_end) continue;
-    // S^T = K Q^T and dP^T = V dO^T, the two products' MFMAs alternating,
-    // each LDS operand read kPipe MFMAs ahead
-    f32x16 S[NST], dP[NST];
-    {
-      auto load = [&](auto jc) -> u32x4 {
-        constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
-        if constexpr (j % 2) return lds_read16(Vs + (32 * st + li) * VST + 16 * kk + 8 * lh);
-        else return lds_read16(Ks + (32 * st + li) * KST + 16 * kk + 8 * lh);
-      };
-      auto mfma = [&](auto jc, u32x4 a) {
-        constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
-        if constexpr (j % 2) dP[st] = E::mfma(a, gr[kk], kk == 0 ? f32x16{} : dP[st]);
-        else S[st] = E::mfma(a, qr[kk], kk == 0 ? f32x16{} : S[st]);
-      };
-      m_pipeline<2 * NST * KSTEPS, kPipe>(load, mfma);
-    }
-    // lane = query row; register r of sub-tile st is key t*BN + 32 st + 8 (r/4) + 4 lh + r%4
-    u32x4 db[NST][2];
-    // every pair of the tile is admissible for this wave when all its rows
-    // and keys exist and (causal) the tile's last key is at or below the
-    // wave's first row's diagonal: the mask is then left out.  Every exp2 is
-    // evaluated and masked pairs are selected to 0, so the loop has no branch.
-    const bool full = rw0 + 32 <= Sq && (t + 1) * BN <= Sk && (!CAUSAL || t * BN + BN - 1 <= rw0 + kv_off);
-    auto grad = [&](auto mask_c) {
-      constexpr bool MASK = decltype(mask_c)::value;
+  auto run = [&](auto lag_c) {
+    constexpr int LAG = decltype(lag_c)::value;
+    f32x16 S[NST], dP[NST];  // the tile between its M and V steps
+    u32x4 db[NST][2];        // dS of the tile between its V and next M steps
 #pragma unroll
-      for (int st = 0; st < NST; ++st) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = t * BN + 32 * st + 8 * (r >> 2) + 4 * lh + (r & 3);
-          const bool ok = !MASK || (row < Sq && key < Sk && (!CAUSAL || key <= row + kv_off));
-          const float e = fast_exp2(__builtin_fmaf(S[st][r], c, -lse2));
-          const float pr = ok ? e : 0.f;
-          S[st][r] = pr * (dP[st][r] - dr);
+    for (int st = 0; st < NST; ++st) {
+      S[st] = f32x16{};
+      dP[st] = f32x16{};
+    }
+    auto needed = [&](int t) { return t >= 0 && t < ntiles && t * BN < wave_end; };
+    const int nphase = ntiles > 0 ? 2 * ntiles + 2 : 0;
+    auto phase = [&](int g, auto kind_c) {
+      constexpr int KIND = decltype(kind_c)::value;
+      const int step = g - LAG;
+      const int t = step >> 1;
+      // copies: K(X) by the leading group in phase 2X - 1, V(X) by the
+      // following group in phase 2X - 2 (both V phases of their group)
+      const int Xk = (g + 1) >> 1, Xv = (g >> 1) + 1;
+      bool do_load = false;
+      if constexpr (KIND == 1) {
+        if (LAG == 0 && (g & 1) && Xk < ntiles) {
+          copy(Xk);
+          do_load = true;
         }
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          const int r0 = 8 * kk;
-          db[st][kk] = u32x4{E::pack2(S[st][r0 + 0], S[st][r0 + 1]), E::pack2(S[st][r0 + 2], S[st][r0 + 3]),
-                             E::pack2(S[st][r0 + 4], S[st][r0 + 5]), E::pack2(S[st][r0 + 6], S[st][r0 + 7])};
+        if (LAG == 1 && !(g & 1) && Xv < ntiles) {
+          copy(Xv);
+          do_load = true;
         }
       }
+      if (KIND == 0 && step >= 0) {
+        // ---- M(t): dQ of tile t - 1, then S and dP of tile t
+        if (needed(t - 1)) {
+          const uint16_t* Kb = Ks + ((t - 1) % 3) * KT;
+          auto load = [&](auto jc) -> u32x4 {
+            constexpr int j = decltype(jc)::value, dt = j % DTILES, kk = (j / DTILES) % 2;
+            constexpr int st = j / (2 * DTILES);
+            const uint16_t* kr = Kb + v_lane + (32 * st + 16 * kk) * KST + 32 * dt;
+            const u32x2 lo = lds_read_tr16(kr), hi = lds_read_tr16(kr + 8 * KST);
+            return u32x4{lo[0], lo[1], hi[0], hi[1]};
+          };
+          auto mfma = [&](auto jc, u32x4 a) {
+            constexpr int j = decltype(jc)::value, dt = j % DTILES, kk = (j / DTILES) % 2;
+            constexpr int st = j / (2 * DTILES);
+            dq[dt] = E::mfma(a, db[st][kk], dq[dt]);
+          };
+          m_pipeline<2 * NST * DTILES, kPipe>(load, mfma);
+        }
+        if (needed(t)) {
+          const uint16_t* Kb = Ks + (t % 3) * KT;
+          const uint16_t* Vb = Vs + (t % 2) * VT;
+          // S^T = K Q^T and dP^T = V dO^T, alternating
+          auto load = [&](auto jc) -> u32x4 {
+            constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
+            if constexpr (j % 2) return lds_read16(Vb + (32 * st + li) * VST + 16 * kk + 8 * lh);
+            else return lds_read16(Kb + (32 * st + li) * KST + 16 * kk + 8 * lh);
+          };
+          auto mfma = [&](auto jc, u32x4 a) {
+            constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
+            if constexpr (j % 2) dP[st] = E::mfma(a, gr[kk], kk == 0 ? f32x16{} : dP[st]);
+            else S[st] = E::mfma(a, qr[kk], kk == 0 ? f32x16{} : S[st]);
+          };
+          m_pipeline<2 * NST * KSTEPS, kPipe>(load, mfma);
+        }
+      } else if (KIND == 1 && step >= 0 && needed(t)) {
+        // ---- V(t): lane = query row; register r of sub-tile st is key
+        // t*BN + 32 st + 8 (r/4) + 4 lh + r%4.  Every exp2 is evaluated and
+        // masked pairs are selected to 0 (no branch).
+        const bool full = rw0 + 32 <= Sq && (t + 1) * BN <= Sk &&
+                          (!CAUSAL || t * BN + BN - 1 <= rw0 + kv_off);
+        auto grad = [&](auto mask_c) {
+          constexpr bool MASK = decltype(mask_c)::value;
+#pragma unroll
+          for (int st = 0; st < NST; ++st) {
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = t * BN + 32 * st + 8 * (r >> 2) + 4 * lh + (r & 3);
+              const bool ok = !MASK || (row < Sq && key < Sk && (!CAUSAL || key <= row + kv_off));
+              const float e = fast_exp2(__builtin_fmaf(S[st][r], c, -lse2));
+              const float pr = ok ? e : 0.f;
+              S[st][r] = pr * (dP[st][r] - dr);
+            }
+#pragma unroll
+            for (int kk = 0; kk < 2; ++kk) {
+              const int r0 = 8 * kk;
+              db[st][kk] = u32x4{E::pack2(S[st][r0 + 0], S[st][r0 + 1]),
+                                 E::pack2(S[st][r0 + 2], S[st][r0 + 3]),
+                                 E::pack2(S[st][r0 + 4], S[st][r0 + 5]),
+                                 E::pack2(S[st][r0 + 6], S[st][r0 + 7])};
+            }
+          }
+        };
+        if (full) grad(std::false_type{});
+        else grad(std::true_type{});
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      if (do_load) wait_vmem();
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
     };
-    if (full) grad(std::false_type{});
-    else grad(std::true_type{});
-    // dQ^T += K^T dS^T: K^T by transposing reads, keys in dS's register
-    // order; MFMA j = (sub-tile st, k-step kk, column tile dt)
-    {
-      auto load = [&](auto jc) -> u32x4 {
-        constexpr int j = decltype(jc)::value, dt = j % DTILES, kk = (j / DTILES) % 2;
-        constexpr int st = j / (2 * DTILES);
-        const uint16_t* kr = Ks + v_lane + (32 * st + 16 * kk) * KST + 32 * dt;
-        const u32x2 lo = lds_read_tr16(kr), hi = lds_read_tr16(kr + 8 * KST);
-        return u32x4{lo[0], lo[1], hi[0], hi[1]};
-      };
-      auto mfma = [&](auto jc, u32x4 a) {
-        constexpr int j = decltype(jc)::value, dt = j % DTILES, kk = (j / DTILES) % 2;
-        constexpr int st = j / (2 * DTILES);
-        dq[dt] = E::mfma(a, db[st][kk], dq[dt]);
-      };
-      m_pipeline<2 * NST * DTILES, kPipe>(load, mfma);
+    using K0 = std::integral_constant<int, LAG>;
+    using K1 = std::integral_constant<int, 1 - LAG>;
+    for (int g = 0; g < nphase; g += 2) {
+      phase(g, K0{});
+      phase(g + 1, K1{});
     }
-  }
+  };
+  if (lead) run(std::integral_constant<int, 0>{});
+  else run(std::integral_constant<int, 1>{});
 
   // dQ = scale * (dS K): lane row li, d = 32 dt + 8 (r/4) + 4 lh + r%4
   if (row < Sq) {
@@ -615,20 +649,20 @@ template <int D, int DT, bool CAUSAL>
 hipError_t launch_bwd_c(const BwdParams& p, hipStream_t stream) {
   // Sq = 0 still writes dK = dV = 0, Sk = 0 still writes dQ = 0
   const long long rows = (long long)p.B * p.Hq * p.Sq;
-  const int nqb = (p.Sq + 127) / 128, nkb = (p.Sk + 127) / 128;
   if (rows > 0) {
     hipLaunchKernelGGL((bwd_pre_kernel<D, DT>), dim3((unsigned)((rows + 31) / 32)), dim3(256), 0,
                        stream, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
+    const int nqb = (p.Sq + 32 * kDqWaves - 1) / (32 * kDqWaves);
     hipLaunchKernelGGL((bwd_dq_kernel<D, DT, CAUSAL>), dim3(p.B * p.Hq * nqb),
-                       dim3(kBwdWaves * 64), 0, stream, p);
+                       dim3(kDqWaves * 64), 0, stream, p);
     const hipError_t e2 = hipGetLastError();
     if (e2 != hipSuccess) return e2;
   }
-  const int nkb2 = (p.Sk + kDkdvKeys - 1) / kDkdvKeys;
-  if (nkb2 > 0 && p.B * p.Hkv > 0)
-    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, CAUSAL>), dim3(p.B * p.Hkv * nkb2),
+  const int nkb = (p.Sk + kDkdvKeys - 1) / kDkdvKeys;
+  if (nkb > 0 && p.B * p.Hkv > 0)
+    hipLaunchKernelGGL((bwd_dkdv_kernel<D, DT, CAUSAL>), dim3(p.B * p.Hkv * nkb),
                        dim3(kDkdvWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
