@@ -118,7 +118,7 @@ fa_status_t plan_prefill(int B, int Hq, int Hkv, int Sq, int Sk, int D, int caus
   // all heads (query-block-major, no XCD dealing): measured on the causal
   // B=1 Hq=128 Hkv=8 S=8192 shape, 0.5-1% faster than the kv-head-major
   // list, static or queued.
-  if (persistent && items >= (long long)kQueueMinItemsPerCTA * NP) {
+  if (dense && persistent && items >= (long long)kQueueMinItemsPerCTA * NP) {
     plan->queue = 1;
     plan->hkv_major = 0;
     plan->xcd_map = 0;

@@ -352,10 +352,11 @@ __device__ __forceinline__ void varlen_item(const PrefillParams& p, const uint16
   }
 }
 
-template <int D, int DT, bool CAUSAL, bool LSE, bool VARLEN, bool SPLIT>
+template <int D, int DT, bool CAUSAL, bool LSE, bool VARLEN, bool SPLIT, bool PF>
 __global__ __launch_bounds__(kPrefillWaves * 64) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void prefill_kernel(PrefillParams p) {
   static_assert(!(SPLIT && VARLEN), "the key split is for the dense layout");
+  static_assert(!(PF && (SPLIT || VARLEN)), "the prefetch and work queue are for dense launches");
   using E = Elt<DT>;
   constexpr int NT = kPrefillWaves * 64;
   constexpr int BM = kPrefillBM;
@@ -496,12 +497,13 @@ void prefill_kernel(PrefillParams p) {
         qr[kk] = p.q_sign < 0 ? (qr[kk] ^ 0x80008000u) : u32x4{0u, 0u, 0u, 0u};
     }
   };
-  // Cross-item prefetch (persistent grids, two-slot rings): in its last
+  // Cross-item prefetch (the PF instances: persistent grids with the work
+  // queue, two-slot rings): in its last
   // phases an item loads the next item's Q and copies its first K/V tile,
   // each wave group into the ring slot it would fill with the item's own
   // tile ntiles, so the next item starts without a prologue.  The ring numbering carries
   // on across items: tile t of an item sits in slot (t + ring) % NBUF.
-  constexpr bool kPrefetch = NBUF == 2 && !SPLIT;
+  constexpr bool kPrefetch = PF && NBUF == 2;
   bool have_pf = false;  // this item's Q and tile 0 were loaded by the one before
   int ring = 0;
   // Work queue (persistent launches with the prefetch): a workgroup's first
@@ -952,24 +954,30 @@ void prefill_kernel(PrefillParams p) {
   }
 }
 
-template <int D, int DT, bool CAUSAL, bool LSE, bool VARLEN, bool SPLIT>
+template <int D, int DT, bool CAUSAL, bool LSE, bool VARLEN, bool SPLIT, bool PF>
 hipError_t launch_one(const PrefillParams& p, int grid, hipStream_t stream) {
-  hipLaunchKernelGGL((prefill_kernel<D, DT, CAUSAL, LSE, VARLEN, SPLIT>), dim3(grid),
+  hipLaunchKernelGGL((prefill_kernel<D, DT, CAUSAL, LSE, VARLEN, SPLIT, PF>), dim3(grid),
                      dim3(kPrefillWaves * 64), 0, stream, p);
   return hipGetLastError();
 }
 
+// Instances: varlen; dense with the key split; dense persistent with the work
+// queue and the cross-item prefetch (measured to pay only together, on long
+// launches); and the plain dense kernel for everything else
 template <int D, int DT, bool CAUSAL>
 hipError_t launch_c(const PrefillParams& p, int grid, hipStream_t stream) {
   const bool lse = p.lse != nullptr;
   if (p.cu_q != nullptr)
-    return lse ? launch_one<D, DT, CAUSAL, true, true, false>(p, grid, stream)
-               : launch_one<D, DT, CAUSAL, false, true, false>(p, grid, stream);
+    return lse ? launch_one<D, DT, CAUSAL, true, true, false, false>(p, grid, stream)
+               : launch_one<D, DT, CAUSAL, false, true, false, false>(p, grid, stream);
   if (p.split_tiles > 0)
-    return lse ? launch_one<D, DT, CAUSAL, true, false, true>(p, grid, stream)
-               : launch_one<D, DT, CAUSAL, false, false, true>(p, grid, stream);
-  return lse ? launch_one<D, DT, CAUSAL, true, false, false>(p, grid, stream)
-             : launch_one<D, DT, CAUSAL, false, false, false>(p, grid, stream);
+    return lse ? launch_one<D, DT, CAUSAL, true, false, true, false>(p, grid, stream)
+               : launch_one<D, DT, CAUSAL, false, false, true, false>(p, grid, stream);
+  if (p.queue != nullptr && p.persistent)
+    return lse ? launch_one<D, DT, CAUSAL, true, false, false, true>(p, grid, stream)
+               : launch_one<D, DT, CAUSAL, false, false, false, true>(p, grid, stream);
+  return lse ? launch_one<D, DT, CAUSAL, true, false, false, false>(p, grid, stream)
+             : launch_one<D, DT, CAUSAL, false, false, false, false>(p, grid, stream);
 }
 
 template <int D, int DT>
