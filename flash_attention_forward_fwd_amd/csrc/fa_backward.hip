@@ -27,8 +27,22 @@ namespace fa {
 namespace {
 
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int kRowPad = 8;          // pad of tiles read by 16-byte row reads only
-constexpr int kTrPad = 32;          // pad of tiles that are also read transposed
+// LDS rows of every tile are padded to D + 8 elements.  A 16-byte row read
+// serves 16 lanes of consecutive rows per pass; at this stride their rows
+// start on distinct 4-bank groups of the 128 banks, so row reads never
+// conflict.  Tiles that are also read by the transposing read (8 consecutive
+// rows of 64 bytes per instruction, which need 8 disjoint 16-bank groups)
+// keep row r of each 32-row block at position tr_pos(r) = 4 (r % 8) + r / 8:
+// the 8 rows of a transposing read then sit 4 positions apart, 16 banks
+// apart, and any 16 consecutive rows still fall on 16 distinct positions
+// mod 32, so neither read conflicts.  Offsets of both reads stay
+// compile-time constants on top of a per-lane base (row r of a transposing
+// read is 16 kk + 8 h + e with e = 0..7 the lane's: position 4 e + 2 kk + h).
+constexpr int kRowPad = 8;
+__device__ __forceinline__ int tr_pos(int r) { return 32 * (r >> 5) + 4 * (r & 7) + ((r >> 3) & 3); }
+__device__ __forceinline__ int tr_row(int pos) {
+  return 32 * (pos >> 5) + 8 * (pos & 3) + ((pos >> 2) & 7);
+}
 // MFMAs an LDS operand read runs ahead of its use
 #ifndef FA_BWD_PIPE
 #define FA_BWD_PIPE 4
@@ -101,9 +115,10 @@ void bwd_dq_kernel(BwdParams p) {
   constexpr int BN = kDqKeys;            // keys per K/V tile (32-key sub-tiles)
   constexpr int NST = BN / 32;
   constexpr int KSTEPS = D / 16, DTILES = D / 32;
-  constexpr int KST = D + kTrPad;        // K: row reads (S) and transposed reads (dQ)
+  constexpr int KST = D + kRowPad;       // K: row reads (S) and transposed reads (dQ), tr_pos order
   constexpr int VST = D + kRowPad;       // V: row reads (dP)
   constexpr int KRC = KST / 8, VRC = VST / 8;
+  static_assert(KRC == VRC, "K and V images share their copy offsets");
   // 1 KiB pieces per tile image, rounded up: the chunks past the tile's BN
   // rows land in the slot's tail and are never read
   constexpr int KNI = (BN * KRC + 63) / 64, VNI = (BN * VRC + 63) / 64;
@@ -155,7 +170,9 @@ void bwd_dq_kernel(BwdParams p) {
   }
   if (rw0 >= Sq) wave_end = 0;
   const int ntiles = (kv_end + BN - 1) / BN;
-  const int v_lane = (4 * lh + (ti >> 2)) * KST + 16 * ((lane >> 4) & 1) + 4 * (ti & 3);
+  // the transposing read's lane base: row e = 4 lh + ti / 4 of 8 at position 4 e
+  const int v_lane = 4 * (4 * lh + (ti >> 2)) * KST + 16 * ((lane >> 4) & 1) + 4 * (ti & 3);
+  const int k_row = tr_pos(li) * KST + 8 * lh;  // row li of a 32-key sub-tile
 
   // tile copies: the leading group copies K images, the following group V
   const int kv_bytes = Sk > 0 ? Sk * D * 2 : 0;
@@ -167,13 +184,15 @@ void bwd_dq_kernel(BwdParams p) {
       (short)0, kv_bytes, kBufferFlags);
   const bool lead = grp == 0;
   constexpr int NPW = KPW > VPW ? KPW : VPW;
+  // image chunk c: LDS row c / KRC (K: the position of key tr_row of it),
+  // column c % KRC; the slot's tail past BN rows reads zeros
   unsigned offs[NPW];
 #pragma unroll
   for (int u = 0; u < NPW; ++u) {
-    const int rc = lead ? KRC : VRC;
     const int cidx = 64 * (gw + 4 * u) + lane;
-    const int rr = cidx / rc, cc = cidx - rr * rc;
-    offs[u] = cc < D / 8 ? (unsigned)((rr * D + cc * 8) * 2) : kPastEnd;
+    const int pos = cidx / KRC, cc = cidx - pos * KRC;
+    const int rr = lead ? tr_row(pos) : pos;
+    offs[u] = (pos < BN && cc < D / 8) ? (unsigned)((rr * D + cc * 8) * 2) : kPastEnd;
   }
   auto copy = [&](int X) {
     if (lead) {
@@ -232,8 +251,8 @@ void bwd_dq_kernel(BwdParams p) {
           auto load = [&](auto jc) -> u32x4 {
             constexpr int j = decltype(jc)::value, dt = j % DTILES, kk = (j / DTILES) % 2;
             constexpr int st = j / (2 * DTILES);
-            const uint16_t* kr = Kb + v_lane + (32 * st + 16 * kk) * KST + 32 * dt;
-            const u32x2 lo = lds_read_tr16(kr), hi = lds_read_tr16(kr + 8 * KST);
+            const uint16_t* kr = Kb + v_lane + (32 * st + 2 * kk) * KST + 32 * dt;
+            const u32x2 lo = lds_read_tr16(kr), hi = lds_read_tr16(kr + KST);
             return u32x4{lo[0], lo[1], hi[0], hi[1]};
           };
           auto mfma = [&](auto jc, u32x4 a) {
@@ -250,7 +269,7 @@ void bwd_dq_kernel(BwdParams p) {
           auto load = [&](auto jc) -> u32x4 {
             constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
             if constexpr (j % 2) return lds_read16(Vb + (32 * st + li) * VST + 16 * kk + 8 * lh);
-            else return lds_read16(Kb + (32 * st + li) * KST + 16 * kk + 8 * lh);
+            else return lds_read16(Kb + k_row + 32 * st * KST + 16 * kk);
           };
           auto mfma = [&](auto jc, u32x4 a) {
             constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
@@ -350,13 +369,13 @@ void bwd_dkdv_kernel(BwdParams p) {
   constexpr int BM = 32;                 // query rows per tile
   constexpr int KSTEPS = D / 16, DTILES = D / 32;
   constexpr int KST = D + kRowPad;       // K, V rows: 16-byte row reads only
-  constexpr int QST = D + kTrPad;        // Q, dO rows: row reads and transposed reads
+  constexpr int QST = D + kRowPad;       // Q, dO rows: row and transposed reads, tr_pos order
   constexpr int KV = kDkdvKeys * KST;    // elements of the block's K (or V)
-  constexpr int TILE = BM * QST;         // elements of one Q (or dO) tile
   constexpr int KRC = KST / 8, QRC = QST / 8;       // 16-byte chunks per LDS row
   constexpr int KNI = kDkdvKeys * KRC / 64;         // 1 KiB pieces of a K (or V) image
-  constexpr int QNI = BM * QRC / 64;                // 1 KiB pieces of a Q (or dO) tile
-  static_assert(kDkdvKeys * KRC % 64 == 0 && BM * QRC % 64 == 0, "images are whole KiB");
+  constexpr int QNI = (BM * QRC + 63) / 64;         // 1 KiB pieces of a Q (or dO) tile, rounded up
+  constexpr int TILE = QNI * 512;                   // elements of one Q (or dO) slot
+  static_assert(kDkdvKeys * KRC % 64 == 0, "K and V images are whole KiB");
   constexpr int NPW = (2 * QNI + 3) / 4;            // tile pieces per wave of a group
   // LDS: K, V | Q tiles [group][slot] | dO tiles [group][slot] | LSE, D [group][slot][64]
   constexpr int Q_OFF = 2 * KV, G_OFF = Q_OFF + 4 * TILE, LD_OFF = G_OFF + 4 * TILE;
@@ -422,8 +441,8 @@ void bwd_dkdv_kernel(BwdParams p) {
     const int pc = gw + 4 * i;
     const int pp = pc < QNI ? pc : pc - QNI;
     const int cidx = 64 * pp + lane;
-    const int rr = cidx / QRC, cc = cidx - rr * QRC;
-    toff[i] = cc < D / 8 ? (unsigned)((rr * D + cc * 8) * 2) : kPastEnd;
+    const int pos = cidx / QRC, cc = cidx - pos * QRC;
+    toff[i] = (pos < BM && cc < D / 8) ? (unsigned)((tr_row(pos) * D + cc * 8) * 2) : kPastEnd;
   }
   // copy this group's tile t into ring slot t % 2 (the group's 4 waves), with
   // the rows' LSE and D (wave gw == 0, 64 rows from r0, those past Sq zero)
@@ -468,7 +487,9 @@ void bwd_dkdv_kernel(BwdParams p) {
     dk[dt] = f32x16{};
     dv[dt] = f32x16{};
   }
-  const int v_lane = (4 * lh + (ti >> 2)) * QST + 16 * ((lane >> 4) & 1) + 4 * (ti & 3);
+  // the transposing read's lane base: row e = 4 lh + ti / 4 of 8 at position 4 e
+  const int v_lane = 4 * (4 * lh + (ti >> 2)) * QST + 16 * ((lane >> 4) & 1) + 4 * (ti & 3);
+  const int q_row = tr_pos(li) * QST + 8 * lh;  // row li of a tile
   // the wave's keys as B operands: key kw0 + li, d = 16 kk + 8 lh + e
   const uint16_t* const kb_row = Ks + (32 * gw + li) * KST + 8 * lh;
   const uint16_t* const vb_row = Vs + (32 * gw + li) * KST + 8 * lh;
@@ -506,8 +527,8 @@ void bwd_dkdv_kernel(BwdParams p) {
           // MFMA j: (k-step kk, column tile dt), dV (j even) or dK
           auto load = [&](auto jc) -> u32x4 {
             constexpr int j = decltype(jc)::value, dt = (j / 2) % DTILES, kk = j / (2 * DTILES);
-            const uint16_t* src = ((j % 2) ? Qb : Gb) + v_lane + 16 * kk * QST + 32 * dt;
-            const u32x2 lo = lds_read_tr16(src), hi = lds_read_tr16(src + 8 * QST);
+            const uint16_t* src = ((j % 2) ? Qb : Gb) + v_lane + 2 * kk * QST + 32 * dt;
+            const u32x2 lo = lds_read_tr16(src), hi = lds_read_tr16(src + QST);
             return u32x4{lo[0], lo[1], hi[0], hi[1]};
           };
           auto mfma = [&](auto jc, u32x4 a) {
@@ -519,8 +540,8 @@ void bwd_dkdv_kernel(BwdParams p) {
         }
         if (qk) {
           const int sl = t & 1;
-          const uint16_t* Qb = lds + Q_OFF + (grp * 2 + sl) * TILE + li * QST + 8 * lh;
-          const uint16_t* Gb = lds + G_OFF + (grp * 2 + sl) * TILE + li * QST + 8 * lh;
+          const uint16_t* Qb = lds + Q_OFF + (grp * 2 + sl) * TILE + q_row;
+          const uint16_t* Gb = lds + G_OFF + (grp * 2 + sl) * TILE + q_row;
           // S = Q K^T and dP = dO V^T, alternating; both operands from LDS,
           // read together kPipe MFMAs ahead
           auto load = [&](auto jc) -> OpPair {
