@@ -131,10 +131,14 @@ void bwd_dq_kernel(BwdParams p) {
   const int wave = uniform(tid >> 6);
   const int li = lane & 31, lh = lane >> 5, ti = lane & 15;
   const int grp = wave >> 2, gw = wave & 3;
-  // items heaviest first: query block level descending, then batch and head
+  // items heaviest first: query block level descending, then batch and head.
+  // Workgroup i runs on XCD i % kXcds; each XCD gets a contiguous run of the
+  // level's (batch, head) items, so the query heads of a kv head run on one
+  // XCD and stream its K/V through one L2
   const int nqb = (p.Sq + BM - 1) / BM;
   const int per_lvl = p.B * p.Hq;
-  const int lvl = (int)blockIdx.x / per_lvl, rr0 = (int)blockIdx.x - lvl * per_lvl;
+  const int lvl = (int)blockIdx.x / per_lvl, pos = (int)blockIdx.x - lvl * per_lvl;
+  const int rr0 = per_lvl % kXcds == 0 ? (pos % kXcds) * (per_lvl / kXcds) + pos / kXcds : pos;
   const int qb = nqb - 1 - lvl, b = rr0 / p.Hq, hq = rr0 - b * p.Hq;
   const int hk = hq / p.gqa;
   const int q0 = qb * BM, rw0 = q0 + wave * 32, row = rw0 + li;
@@ -347,7 +351,8 @@ struct OpPair {
 // ---- dkdv: one workgroup of 8 waves per (batch, kv head, 128 keys) ---------------
 // Waves w and w + 4 own the same 32 keys (K and V rows of the block stay in
 // LDS, read as B operands) and take alternate 32-row query tiles of the
-// (query head of the group, row tile) list: the leading group (waves 0-3) the
+// (row tile, query head of the group) list, row tiles from the last down and
+// heads innermost: the leading group (waves 0-3) the
 // even tiles, the following group the odd ones.  The two groups run the
 // forward's ping-pong one phase apart, so the wave pair of a SIMD alternates
 // MFMA and vector work:
@@ -403,16 +408,20 @@ void bwd_dkdv_kernel(BwdParams p) {
   (void)nkb;
 
   // row tiles that see a key of this block: row + kv_off >= k0 when causal;
-  // the (query head g of the group, row tile) list, g outermost
+  // the (row tile, query head g of the group) list runs the row tiles from
+  // the last one down with g innermost.  Every key block of a kv head then
+  // starts on the same last row tile and walks the rows in step with the
+  // others, so the workgroups of that kv head read each Q/dO tile at about
+  // the same time and share it in L2 instead of streaming it separately.
   const int r_first = CAUSAL ? (max(0, k0 - kv_off) / BM) * BM : 0;
   const int nrt = r_first < Sq ? (Sq - r_first + BM - 1) / BM : 0;
   const int total = p.gqa * nrt;
   const int n_lead = (total + 1) / 2, n_mine = grp == 0 ? n_lead : total / 2;
   auto tile_row0 = [&](int t) {  // first row of this group's tile t
     const int it = 2 * t + grp;
-    return r_first + (it % nrt) * BM;
+    return r_first + (nrt - 1 - it / p.gqa) * BM;
   };
-  auto tile_head = [&](int t) { return hk * p.gqa + (2 * t + grp) / nrt; };
+  auto tile_head = [&](int t) { return hk * p.gqa + (2 * t + grp) % p.gqa; };
 
   // ---- copies (buffer loads to LDS, 1 KiB pieces; lane j of a load writes
   // bytes [16 j, 16 j + 16) of its piece).  Image chunk c is row c / RC,
