@@ -98,7 +98,8 @@ __global__ __launch_bounds__(256) void bwd_pre_kernel(BwdParams p) {
 // registers as B operands), the two wave groups walk the same 32-key K/V
 // tiles one phase apart:
 //   M(t): dQ^T += K^T dS^T of tile t - 1 (K^T by transposing reads), then
-//         S^T = K Q^T and dP^T = V dO^T of tile t: 24 MFMAs a wave
+//         S^T = K Q^T and dP^T = V dO^T of tile t: 24 MFMAs a wave, one
+//         software pipeline of LDS reads ahead of the MFMAs
 //   V(t): P = exp2(S c - LSE log2 e) masked, dS = P (dP - D), packed, and
 //         the copies of the ring below
 // K(t) is read as rows in phases 2t, 2t + 1 and transposed in 2t + 2, 2t + 3;
@@ -212,6 +213,10 @@ void bwd_dq_kernel(BwdParams p) {
     }
   };
   if (ntiles > 0) copy(0);
+  // the third K slot is first filled in phase 3: zeros until then, so the
+  // dQ half of M(0) multiplies finite values (by a zero dS)
+  for (int i = tid; i < KT / 8; i += kDqWaves * 64)
+    lds_write16(Ks + 2 * KT + 8 * i, u32x4{0u, 0u, 0u, 0u});
   wait_vmem();
   __syncthreads();
 
@@ -227,6 +232,7 @@ void bwd_dq_kernel(BwdParams p) {
     for (int st = 0; st < NST; ++st) {
       S[st] = f32x16{};
       dP[st] = f32x16{};
+      db[st][0] = db[st][1] = u32x4{0u, 0u, 0u, 0u};
     }
     auto needed = [&](int t) { return t >= 0 && t < ntiles && t * BN < wave_end; };
     const int nphase = ntiles > 0 ? 2 * ntiles + 2 : 0;
@@ -249,39 +255,54 @@ void bwd_dq_kernel(BwdParams p) {
         }
       }
       if (KIND == 0 && step >= 0) {
-        // ---- M(t): dQ of tile t - 1, then S and dP of tile t
-        if (needed(t - 1)) {
-          const uint16_t* Kb = Ks + ((t - 1) % 3) * KT;
-          auto load = [&](auto jc) -> u32x4 {
-            constexpr int j = decltype(jc)::value, dt = j % DTILES, kk = (j / DTILES) % 2;
-            constexpr int st = j / (2 * DTILES);
-            const uint16_t* kr = Kb + v_lane + (32 * st + 2 * kk) * KST + 32 * dt;
-            const u32x2 lo = lds_read_tr16(kr), hi = lds_read_tr16(kr + KST);
-            return u32x4{lo[0], lo[1], hi[0], hi[1]};
-          };
-          auto mfma = [&](auto jc, u32x4 a) {
-            constexpr int j = decltype(jc)::value, dt = j % DTILES, kk = (j / DTILES) % 2;
-            constexpr int st = j / (2 * DTILES);
-            dq[dt] = E::mfma(a, db[st][kk], dq[dt]);
-          };
-          m_pipeline<2 * NST * DTILES, kPipe>(load, mfma);
-        }
-        if (needed(t)) {
-          const uint16_t* Kb = Ks + (t % 3) * KT;
-          const uint16_t* Vb = Vs + (t % 2) * VT;
-          // S^T = K Q^T and dP^T = V dO^T, alternating
-          auto load = [&](auto jc) -> u32x4 {
-            constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
-            if constexpr (j % 2) return lds_read16(Vb + (32 * st + li) * VST + 16 * kk + 8 * lh);
-            else return lds_read16(Kb + k_row + 32 * st * KST + 16 * kk);
-          };
-          auto mfma = [&](auto jc, u32x4 a) {
-            constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
-            if constexpr (j % 2) dP[st] = E::mfma(a, gr[kk], kk == 0 ? f32x16{} : dP[st]);
-            else S[st] = E::mfma(a, qr[kk], kk == 0 ? f32x16{} : S[st]);
-          };
-          m_pipeline<2 * NST * KSTEPS, kPipe>(load, mfma);
-        }
+        // ---- M(t): dQ of tile t - 1, then S and dP of tile t, as one
+        // pipeline (the first S/dP operands are read during the last dQ
+        // MFMAs instead of after them)
+        const uint16_t* Kp = Ks + ((t + 2) % 3) * KT;  // K(t - 1)
+        auto load_q = [&](auto jc) -> u32x4 {
+          constexpr int j = decltype(jc)::value, dt = j % DTILES, kk = (j / DTILES) % 2;
+          constexpr int st = j / (2 * DTILES);
+          const uint16_t* kr = Kp + v_lane + (32 * st + 2 * kk) * KST + 32 * dt;
+          const u32x2 lo = lds_read_tr16(kr), hi = lds_read_tr16(kr + KST);
+          return u32x4{lo[0], lo[1], hi[0], hi[1]};
+        };
+        auto mfma_q = [&](auto jc, u32x4 a) {
+          constexpr int j = decltype(jc)::value, dt = j % DTILES, kk = (j / DTILES) % 2;
+          constexpr int st = j / (2 * DTILES);
+          dq[dt] = E::mfma(a, db[st][kk], dq[dt]);
+        };
+        const uint16_t* Kb = Ks + (t % 3) * KT;
+        const uint16_t* Vb = Vs + (t % 2) * VT;
+        // S^T = K Q^T and dP^T = V dO^T, alternating
+        auto load_s = [&](auto jc) -> u32x4 {
+          constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
+          if constexpr (j % 2) return lds_read16(Vb + (32 * st + li) * VST + 16 * kk + 8 * lh);
+          else return lds_read16(Kb + k_row + 32 * st * KST + 16 * kk);
+        };
+        auto mfma_s = [&](auto jc, u32x4 a) {
+          constexpr int j = decltype(jc)::value, st = j / (2 * KSTEPS), kk = (j / 2) % KSTEPS;
+          if constexpr (j % 2) dP[st] = E::mfma(a, gr[kk], kk == 0 ? f32x16{} : dP[st]);
+          else S[st] = E::mfma(a, qr[kk], kk == 0 ? f32x16{} : S[st]);
+        };
+        // Both halves run in every M step (one code path keeps the
+        // register allocation at two waves per SIMD without spills).  A dQ
+        // half without a tile t - 1 adds exact zeros: dS is zero until the
+        // first V step and is zeroed by every V step whose tile this wave
+        // skips, and the K slot it reads holds finite data (K tiles, or the
+        // zeros the third slot starts with).  S and dP of a tile the wave
+        // does not need are never read.
+        constexpr int NQ = 2 * NST * DTILES, NS = 2 * NST * KSTEPS;
+        auto load = [&](auto jc) -> u32x4 {
+          constexpr int j = decltype(jc)::value;
+          if constexpr (j < NQ) return load_q(jc);
+          else return load_s(std::integral_constant<int, j - NQ>{});
+        };
+        auto mfma = [&](auto jc, u32x4 a) {
+          constexpr int j = decltype(jc)::value;
+          if constexpr (j < NQ) mfma_q(jc, a);
+          else mfma_s(std::integral_constant<int, j - NQ>{}, a);
+        };
+        m_pipeline<NQ + NS, kPipe>(load, mfma);
       } else if (KIND == 1 && step >= 0 && needed(t)) {
         // ---- V(t): lane = query row; register r of sub-tile st is key
         // t*BN + 32 st + 8 (r/4) + 4 lh + r%4.  Every exp2 is evaluated and
@@ -312,6 +333,10 @@ void bwd_dq_kernel(BwdParams p) {
         };
         if (full) grad(std::false_type{});
         else grad(std::true_type{});
+      } else if (KIND == 1 && step >= 0) {
+        // a tile this wave skips: the next M step's dQ half adds zeros
+#pragma unroll
+        for (int st = 0; st < NST; ++st) db[st][0] = db[st][1] = u32x4{0u, 0u, 0u, 0u};
       }
       __builtin_amdgcn_sched_barrier(0);
       if (do_load) wait_vmem();
