@@ -45,7 +45,7 @@
 //                   order in which P sits in its registers.
 // K and V of a chunk are copied global -> LDS by 16-byte buffer loads that
 // write LDS directly and bypass the caches' retention (nontemporal: each byte
-// is read once), two chunks in flight per wave.
+// is read once); a wave's next chunk is in flight while it computes one.
 #include <mutex>
 
 #include "fa_common.h"
