@@ -540,6 +540,11 @@ void bwd_dkdv_kernel(BwdParams p) {
 
   f32x16 S, dP;         // the tile between its M and V steps
   u32x4 pb[2], db[2];   // P and dS of the tile between its V and next M steps
+  // the LSE and D of the rows of registers 0-7 of the tile between its M and
+  // V steps: read from LDS at the start of the M step, whose MFMAs hide the
+  // read's latency (the LDS queue is long while the other group's M step
+  // streams its operands)
+  f32x4 lse_a[2] = {}, d_a[2] = {};
   S = f32x16{};
   dP = f32x16{};
   auto run = [&](auto lag_c) {
@@ -554,6 +559,14 @@ void bwd_dkdv_kernel(BwdParams p) {
       if (KIND == 0 && step >= 0) {
         // ---- M(t)
         const bool pv = needed(t - 1), qk = needed(t);
+        if (qk) {
+          const float* l = LD + ((grp * 2 + (t & 1)) * 2) * 64;
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            lse_a[q] = *reinterpret_cast<const f32x4*>(l + 8 * q + 4 * lh);
+            d_a[q] = *reinterpret_cast<const f32x4*>(l + 64 + 8 * q + 4 * lh);
+          }
+        }
         if (pv) {
           const int sl = (t - 1) & 1;
           const uint16_t* Gb = lds + G_OFF + (grp * 2 + sl) * TILE;
@@ -591,22 +604,20 @@ void bwd_dkdv_kernel(BwdParams p) {
           m_pipeline<2 * KSTEPS, kPairPipe>(load, mfma);
         }
       } else if (KIND == 1 && step >= 0) {
-        // ---- V(t): the rows' LSE and D first (LDS reads before this phase's
-        // copy is issued), then the copy of tile t + 1, then the gradient math
+        // ---- V(t): the LSE and D of the rows of registers 8-15 (LDS reads
+        // before this phase's copy is issued; those of registers 0-7 came
+        // with the M step), then the copy of tile t + 1, then the gradient math
         const bool use = needed(t);
         const int r0 = tile_row0(t), sl = t & 1;
         const float* l = LD + ((grp * 2 + sl) * 2) * 64;
-        // the rows' LSE and D of the first half (registers 0-7) before this
-        // phase's copy is issued, the second half's after the first half's math
-        f32x4 lse4[2], d4[2];
-        auto read_ld = [&](int half) {
+        f32x4 lse_b[2], d_b[2];
+        if (use) {
 #pragma unroll
           for (int q = 0; q < 2; ++q) {
-            lse4[q] = *reinterpret_cast<const f32x4*>(l + 16 * half + 8 * q + 4 * lh);
-            d4[q] = *reinterpret_cast<const f32x4*>(l + 64 + 16 * half + 8 * q + 4 * lh);
+            lse_b[q] = *reinterpret_cast<const f32x4*>(l + 16 + 8 * q + 4 * lh);
+            d_b[q] = *reinterpret_cast<const f32x4*>(l + 64 + 16 + 8 * q + 4 * lh);
           }
-        };
-        if (use) read_ld(0);
+        }
         if (t + 1 < n_mine) {
           copy_tile(t + 1);
           do_load = true;
@@ -615,7 +626,7 @@ void bwd_dkdv_kernel(BwdParams p) {
           // lane = key; register r is query row r0 + 8 (r/4) + 4 lh + r%4.  Every
           // exp2 is evaluated and masked pairs are selected to 0 (no branch).
           const bool full = r0 + BM <= Sq && kw0 + 32 <= Sk && (!CAUSAL || kw0 + 31 <= r0 + kv_off);
-          auto grad = [&](auto mask_c, auto half_c) {
+          auto grad = [&](auto mask_c, auto half_c, const f32x4 (&lse4)[2], const f32x4 (&d4)[2]) {
             constexpr bool MASK = decltype(mask_c)::value;
             constexpr int H = decltype(half_c)::value;
 #pragma unroll
@@ -636,12 +647,10 @@ void bwd_dkdv_kernel(BwdParams p) {
           };
           using H0 = std::integral_constant<int, 0>;
           using H1 = std::integral_constant<int, 1>;
-          if (full) grad(std::false_type{}, H0{});
-          else grad(std::true_type{}, H0{});
-          __builtin_amdgcn_sched_barrier(0);
-          read_ld(1);
-          if (full) grad(std::false_type{}, H1{});
-          else grad(std::true_type{}, H1{});
+          if (full) grad(std::false_type{}, H0{}, lse_a, d_a);
+          else grad(std::true_type{}, H0{}, lse_a, d_a);
+          if (full) grad(std::false_type{}, H1{}, lse_b, d_b);
+          else grad(std::true_type{}, H1{}, lse_b, d_b);
         }
       }
       __builtin_amdgcn_sched_barrier(0);
