@@ -290,6 +290,9 @@ __device__ __forceinline__ bool merge_parts(const PrefillParams& p, int w, int p
 // MI355X)", TODO / follow-ups: per-sequence load balance of the varlen path).
 // Every wave derives an item from the per-sequence block counts in LDS.
 constexpr int kVarlenMaxSeqs = 4096;  // batches up to this size use the table
+// block levels up to which the item lookup uses a per-level table in LDS
+// (binary search) instead of walking the levels from the top
+constexpr int kVarlenMaxLevels = 960;
 
 // sequences with more than L query blocks
 __device__ __forceinline__ int seqs_above(const uint16_t* nqb, int B, int L, int lane) {
@@ -324,9 +327,12 @@ __device__ __forceinline__ int nth_seq_above(const uint16_t* nqb, int B, int L, 
 // XCDs' lists are alike) in the block-major order (block level descending,
 // sequence, kv head, group member): sorted by cost, which the snake rounds
 // balance best, while each kv head's K/V stays in one XCD's L2.
+// `above` (LDS, or nullptr): above[L] = (sequence, block) pairs at levels >= L,
+// above[nqb] = 0.  Level L holds the items r with above[L + 1] per <= r <
+// above[L] per.
 __device__ __forceinline__ void varlen_item(const PrefillParams& p, const uint16_t* nqb,
-                                            int total_blocks, int w, int lane, bool xmap, int x,
-                                            int& b, int& hq, int& qb) {
+                                            const int* above, int total_blocks, int w, int lane,
+                                            bool xmap, int x, int& b, int& hq, int& qb) {
   // items per (sequence, block)
   const int per = xmap ? p.Hq / kXcds : (p.hkv_major ? p.gqa : p.Hq);
   int r = w, hk = 0;
@@ -336,10 +342,22 @@ __device__ __forceinline__ void varlen_item(const PrefillParams& p, const uint16
     r = w - hk * per_kv;
   }
   int L = p.nqb - 1;
-  for (; L > 0; --L) {
-    const int n = seqs_above(nqb, p.B, L, lane) * per;
-    if (r < n) break;
-    r -= n;
+  if (above != nullptr) {
+    // the last level L with above[L] per > r (above falls as L rises)
+    int lo = 0, hi = p.nqb - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (above[mid] * per > r) lo = mid;
+      else hi = mid - 1;
+    }
+    L = lo;
+    r -= above[L + 1] * per;
+  } else {
+    for (; L > 0; --L) {
+      const int n = seqs_above(nqb, p.B, L, lane) * per;
+      if (r < n) break;
+      r -= n;
+    }
   }
   const int j = r / per, m = r - j * per;
   b = nth_seq_above(nqb, p.B, L, j, lane);
@@ -396,8 +414,10 @@ void prefill_kernel(PrefillParams p) {
 
   // varlen: query blocks per sequence, and the compacted item count
   __shared__ uint16_t nqb_tab[VARLEN ? kVarlenMaxSeqs : 1];
+  __shared__ int lvl_above[VARLEN ? kVarlenMaxLevels + 1 : 1];
   int work_items = p.work_items, total_blocks = 0;
   const bool compact = VARLEN && p.B <= kVarlenMaxSeqs && p.nqb <= 0xFFFF;
+  const bool lvl = compact && p.nqb <= kVarlenMaxLevels;
   if constexpr (VARLEN) {
     if (compact) {
       for (int i = tid; i < p.B; i += NT) {
@@ -412,6 +432,33 @@ void prefill_kernel(PrefillParams p) {
       for (int o = 32; o > 0; o >>= 1) t += __shfl_xor(t, o);
       total_blocks = uniform(t);
       work_items = total_blocks * p.Hq;
+      if (lvl) {
+        // above[L] = sum over sequences of max(0, blocks - L): a histogram of
+        // the sequences' top levels, then two suffix sums (wave 0)
+        for (int i = tid; i <= p.nqb; i += NT) lvl_above[i] = 0;
+        __syncthreads();
+        for (int i = tid; i < p.B; i += NT)
+          if (nqb_tab[i] > 0) atomicAdd(&lvl_above[min((int)nqb_tab[i], p.nqb) - 1], 1);
+        __syncthreads();
+        if (wave == 0) {
+          for (int pass = 0; pass < 2; ++pass) {
+            int carry = 0;
+            for (int base = ((p.nqb - 1) >> 6) << 6; base >= 0; base -= 64) {
+              const int i = base + lane;
+              int v = i < p.nqb ? lvl_above[i] : 0;
+#pragma unroll
+              for (int o = 1; o < 64; o <<= 1) {
+                const int u = __shfl_down(v, o);
+                v += lane + o < 64 ? u : 0;
+              }
+              v += carry;
+              if (i < p.nqb) lvl_above[i] = v;
+              carry = __shfl(v, 0);
+            }
+          }
+        }
+        __syncthreads();
+      }
     }
   }
 
@@ -441,7 +488,9 @@ void prefill_kernel(PrefillParams p) {
   };
   auto locate = [&](int w, ItemLoc& L) -> bool {
     int b, hq, qb;
-    if (compact) varlen_item(p, nqb_tab, total_blocks, w, lane, xmap, xcd, b, hq, qb);
+    if (compact)
+      varlen_item(p, nqb_tab, lvl ? lvl_above : nullptr, total_blocks, w, lane, xmap, xcd, b, hq,
+                  qb);
     else if (xmap) xcd_item(p, xcd, w, b, hq, qb);
     else decode_item(p, w, b, hq, qb);
     const int hk = hq / p.gqa;
