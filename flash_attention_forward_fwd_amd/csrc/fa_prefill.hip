@@ -975,15 +975,55 @@ void prefill_kernel(PrefillParams p) {
         continue;
     }
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    if (row < Sq) {
-      uint16_t* orow = og + qbase + (long long)row * QRS + 4 * lh;
+    // With 128-key tiles at D = 128 the wave's O rows go through LDS, so that
+    // each global store writes four whole rows instead of 8 bytes of each of
+    // 32 rows.  The staging slot is the ring slot of tile ntiles + 1 (ring
+    // already advanced past this item): the next item's first tile, when it
+    // was prefetched, went to the slot of tile ntiles, a prologue copies into
+    // the slot of tile 0 of the next item (that same slot), and every read of
+    // this item's tiles ended before the last phase's barrier.  The leading
+    // group stages in the K ring, the following group in the V ring, 32 rows
+    // of D + 8 elements per wave (8-byte writes and 16-byte row reads
+    // without bank conflicts).
+    constexpr bool kStagedStore = D == 128 && NBUF == 2;
+    if constexpr (kStagedStore) {
+      constexpr int OST = D + 8;
+      constexpr int LPR = D / 8;        // lanes per row of a store
+      constexpr int RPI = 64 / LPR;     // rows per store
+      static_assert((kPrefillWaves / 2) * 32 * OST <= KTILE && (kPrefillWaves / 2) * 32 * OST <= VTILE,
+                    "four waves' O rows fit a ring slot");
+      const int es = uniform((ring + 1) % NBUF);
+      uint16_t* ob = (wave < kPrefillWaves / 2 ? Ks + es * KTILE : Vs + es * VTILE) +
+                     (wave % (kPrefillWaves / 2)) * 32 * OST;
 #pragma unroll
       for (int dt = 0; dt < DTILES; ++dt) {
 #pragma unroll
         for (int a = 0; a < 4; ++a) {
           const u32x2 pk = {E::pack2(oacc[dt][4 * a + 0] * inv, oacc[dt][4 * a + 1] * inv),
                             E::pack2(oacc[dt][4 * a + 2] * inv, oacc[dt][4 * a + 3] * inv)};
-          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * a) = pk;
+          *reinterpret_cast<u32x2*>(ob + li * OST + 32 * dt + 8 * a + 4 * lh) = pk;
+        }
+      }
+      const int rl = lane / LPR, cl = lane % LPR;
+#pragma unroll
+      for (int j = 0; j < 32 / RPI; ++j) {
+        const int r = RPI * j + rl;
+        const u32x4 v = lds_read16(ob + r * OST + 8 * cl);
+        if (rw0 + r < Sq)
+          *reinterpret_cast<u32x4*>(og + qbase + (long long)(rw0 + r) * QRS + 8 * cl) = v;
+      }
+    }
+    if (row < Sq) {
+      if constexpr (!kStagedStore) {
+        uint16_t* orow = og + qbase + (long long)row * QRS + 4 * lh;
+#pragma unroll
+        for (int dt = 0; dt < DTILES; ++dt) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const u32x2 pk = {E::pack2(oacc[dt][4 * a + 0] * inv, oacc[dt][4 * a + 1] * inv),
+                              E::pack2(oacc[dt][4 * a + 2] * inv, oacc[dt][4 * a + 3] * inv)};
+            *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * a) = pk;
+          }
         }
       }
       if (LSE && lh == 0) {
