@@ -65,6 +65,15 @@ constexpr int kDmaSlots = (kPrefillBN * (128 + kVPad) / 512 + 3) / 4;
 #define FA_RESCALE_TAU 8.0f
 #endif
 constexpr float kRescaleTau = FA_RESCALE_TAU;
+static_assert(kRescaleTau == (float)(int)kRescaleTau && kRescaleTau >= 1.f && kRescaleTau <= 64.f,
+              "the rescale threshold is a whole number of octaves");
+constexpr float pow2_whole(int n) {
+  float r = 1.f;
+  for (int i = 0; i < n; ++i) r *= 2.f;
+  return r;
+}
+// 2^kRescaleTau: no p above it survives a tile
+constexpr float kRescaleGate = pow2_whole((int)kRescaleTau);
 // LDS operand reads run this many MFMAs ahead of their consumer in the
 // steady-state M step (LDS latency under load exceeds two MFMAs)
 #ifndef FA_LOOKAHEAD
@@ -571,9 +580,21 @@ void prefill_kernel(PrefillParams p) {
   __shared__ unsigned q_item[2], q_tick;
   constexpr unsigned kEmpty = 0xFFFFFFFFu, kNoTicket = 0x3FFFFFFFu;
   auto qctr = [&]() { return p.queue + (xmap ? xcd : 0); };
+  // An item whose straight-line softmax overflowed runs again in the next
+  // round (`again`) with the max-first softmax in every phase; such a round
+  // takes no new item (qround counts the rounds that do).
+  __shared__ int redo_item;  // r + 1 when round r's item must run again
+  if (tid == 0) redo_item = 0;
+  bool again = false;
+  int w_again = 0, qround = 0;
   for (int round = 0;; ++round) {
     int w;
-    if (qmode) {
+    const bool safe = again;
+    if (again) {
+      w = w_again;
+      again = false;
+    } else if (qmode) {
+      const int round = qround++;
       w = round == 0 ? cta : uniform((int)q_item[round & 1]);
       if (tid == 0) {
         unsigned nxt = NP + cta;
@@ -588,13 +609,14 @@ void prefill_kernel(PrefillParams p) {
       __syncthreads();
       if (w >= list_items) break;
     } else if (p.persistent) {
+      const int round = qround++;
       if (round * NP >= list_items) break;
       // snake order: even rounds ascend, odd rounds descend, so every CTA
       // pairs a heavy item with a light one
       w = round * NP + ((round & 1) ? (NP - 1 - cta) : cta);
       if (w >= list_items) continue;
     } else {
-      if (round > 0) break;
+      if (qround++ > 0) break;
       w = blockIdx.x;
       if constexpr (SPLIT) {
         split_part<CAUSAL>(p, blockIdx.x, w, part, nparts, t0, t1);
@@ -754,6 +776,57 @@ void prefill_kernel(PrefillParams p) {
       };
       m_pipeline<NPV + NQK, kLookahead>(load, mfma);
     };
+    // V step of the straight-line body in the queue-driven launches: p =
+    // exp2(s c - m) against the current reference first.  Every p is >= 0,
+    // so when no lane's partial row sum exceeds 2^tau no p does, the
+    // reference stands, and the tile's row max is not needed at all.
+    // Otherwise (rare) the max of p decides: a row whose p went above 2^tau
+    // moves its reference up by the binary exponent e of that max and scales
+    // its p, l and O by 2^-e (exact), which leaves every p <= 1; a row without
+    // a reference yet adopts the one its exps used.  An exp that overflowed
+    // leaves l infinite (or NaN): the last phase sees it and the item runs
+    // again with the max-first step (the lost scores cannot be formed here
+    // without registers the kernel does not have).
+    auto stage_fast = [&](f32x16 (&S)[NST], u32x4 (&P)[NST][2]) {
+      const bool fresh = m_run == -__builtin_inff();
+      const float m_use = fresh ? 0.f : m_run;
+      float psum = 0.f;
+#pragma unroll
+      for (int st = 0; st < NST; ++st)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          S[st][r] = fast_exp2(__builtin_fmaf(S[st][r], c, -m_use));
+          psum += S[st][r];
+        }
+      if (__builtin_amdgcn_ballot_w64(!(psum <= kRescaleGate) || fresh)) {
+        float pm = S[0][0];
+#pragma unroll
+        for (int st = 0; st < NST; ++st)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) pm = fmaxf(pm, S[st][r]);
+        pm = pair_max(pm);
+        const int e = pm > kRescaleGate ? __builtin_amdgcn_frexp_expf(pm) : 0;
+        if (__builtin_amdgcn_ballot_w64(e != 0)) {
+          const float a = __builtin_amdgcn_ldexpf(1.0f, -e);
+#pragma unroll
+          for (int st = 0; st < NST; ++st) S[st] *= a;
+          psum *= a;
+          l_run *= a;
+#pragma unroll
+          for (int dt = 0; dt < DTILES; ++dt) oacc[dt] *= a;
+        }
+        m_run = m_use + (float)e;
+      }
+      l_run += psum;
+#pragma unroll
+      for (int st = 0; st < NST; ++st)
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          const int r0 = 8 * kk;
+          P[st][kk] = u32x4{E::pack2(S[st][r0 + 0], S[st][r0 + 1]), E::pack2(S[st][r0 + 2], S[st][r0 + 3]),
+                            E::pack2(S[st][r0 + 4], S[st][r0 + 5]), E::pack2(S[st][r0 + 6], S[st][r0 + 7])};
+        }
+    };
 
     // ---- ping-pong schedule ----------------------------------------------------
     // Each wave runs the step sequence M(0) V(0) M(1) V(1) ... M(ntiles) over
@@ -809,8 +882,8 @@ void prefill_kernel(PrefillParams p) {
     bool pf = false;
     __amdgpu_buffer_rsrc_t krs_n = krs, vrs_n = vrs;
     if constexpr (kPrefetch) {
-      const int nr = round + 1;
-      if (p.persistent && ntiles > 0 && (qmode || nr * NP < list_items)) {
+      const int nr = qround;  // the next round that takes an item
+      if (!safe && p.persistent && ntiles > 0 && (qmode || nr * NP < list_items)) {
         const int wn = qmode ? uniform((int)q_item[nr & 1]) : nr * NP + ((nr & 1) ? (NP - 1 - cta) : cta);
         if (wn < list_items && locate(wn, N)) {
           pf = true;
@@ -823,7 +896,7 @@ void prefill_kernel(PrefillParams p) {
       }
     }
     if constexpr (SPLIT) {
-      if (nparts > 1 && tid == 0) split_word[0] = add_flag(p.split_cnt + 2 * w, 1u);
+      if (!safe && nparts > 1 && tid == 0) split_word[0] = add_flag(p.split_cnt + 2 * w, 1u);
     }
     wait_vmem();
     __syncthreads();
@@ -852,7 +925,7 @@ void prefill_kernel(PrefillParams p) {
           // of the first final phase (ahead of the Q loads, so that waiting
           // for it does not wait for them), written to LDS at the end of the
           // second, so the atomic's round trip overlaps both
-          if (qmode && g == nphase - 2 && tid == 0) q_tk = add_flag(qctr(), 1u);
+          if (qmode && !safe && g == nphase - 2 && tid == 0) q_tk = add_flag(qctr(), 1u);
           if (pf && g == nphase - 2) load_q(N);
         }
         // the leading group copies K(X) in its V phase 2X - 2 NBUF + 3, the
@@ -920,13 +993,24 @@ void prefill_kernel(PrefillParams p) {
                 S[st][r] = off > lim ? -__builtin_inff() : S[st][r];
               }
           }
-          stage_maxn(S);
+          if constexpr (ALL) {
+            stage_fast(S, P);
+          } else {
+            stage_maxn(S);
 #pragma unroll
-          for (int st = 0; st < NST; ++st) stage_exp(S[st], P[st]);
+            for (int st = 0; st < NST; ++st) stage_exp(S[st], P[st]);
+          }
         }
         if constexpr (KIND == 0 && kMfmaPrio > 0) __builtin_amdgcn_s_setprio(0);
         if constexpr (LAST && kPrefetch) {
-          if (qmode && g == nphase - 1 && tid == 0) q_tick = q_tk;
+          if (qmode && !safe && g == nphase - 1 && tid == 0) q_tick = q_tk;
+        }
+        if constexpr (LAST) {
+          // every softmax step of the item is done: an overflowed exp left l
+          // non-finite (seen by all after this phase's barrier)
+          if (!safe && g == nphase - 1 &&
+              __builtin_amdgcn_ballot_w64(!__builtin_isfinite(l_run)))
+            redo_item = round + 1;
         }
         // each phase is its own scheduling region: nothing drifts across the
         // barrier that separates the two waves' roles; the tile copied in
@@ -946,7 +1030,7 @@ void prefill_kernel(PrefillParams p) {
         phase(g, K0{}, F{}, F{});
         phase(g + 1, K1{}, F{}, F{});
       }
-      for (; g + 1 < main_end; g += 2) {
+      for (; g + 1 < (safe ? 0 : main_end); g += 2) {
         phase(g, K0{}, T{}, F{});
         phase(g + 1, K1{}, T{}, F{});
       }
@@ -965,6 +1049,17 @@ void prefill_kernel(PrefillParams p) {
     if constexpr (kPrefetch) {
       have_pf = pf;
       ring = uniform((ring + ntiles) % NBUF);
+    }
+    if (redo_item == round + 1) {
+      // run the item again in the next round, from its own prologue (the
+      // next item's Q and first tile, if prefetched here, are loaded again
+      // after it)
+      wait_vmem();
+      __syncthreads();
+      have_pf = false;
+      again = true;
+      w_again = w;
+      continue;
     }
 
     // ---- epilogue: O = O^T / l, rows < Sq --------------------------------------

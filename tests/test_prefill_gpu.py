@@ -295,6 +295,44 @@ def test_guard_bands_untouched_and_unread():
     assert np.array_equal(out[G:G + q.size].reshape(q.shape), plain)
 
 
+@pytest.mark.parametrize("k0", [24.0, 256.0], ids=["rescaled", "overflowed"])
+def test_score_jump_in_mask_free_tile(k0):
+    # key 700 scores far above every other key for every row (q[:, 0] = 8,
+    # k[700, 0] = k0) and sits in a mask-free tile of the query blocks that
+    # start at rows 1024 and 1280.  With k0 = 24 its exp against the running
+    # reference is about 2^19 (above 2^tau but finite: the row's reference
+    # moves by a power of two); with k0 = 256 the exp overflows and the item
+    # is computed again with the max-first softmax.  Every schedule matches
+    # the oracle; the grid and the queue-driven persistent launch (whole items
+    # both) give the same bits (the automatic plan here splits items' keys
+    # into parts, whose merge rounds differently).
+    fa = _fa()
+    dtype = "bf16"
+    B, Hq, Hkv, S, D = 1, 4, 2, 1536, 128
+    rng = np.random.default_rng(131)
+    qf = rng.standard_normal((B, Hq, S, D)).astype(np.float32)
+    kf = rng.standard_normal((B, Hkv, S, D)).astype(np.float32)
+    qf[..., 0] = 8.0
+    kf[:, :, 700, 0] = k0
+    q, k = wl.to_bits(qf, dtype), wl.to_bits(kf, dtype)
+    v = wl.normal_bits((B, Hkv, S, D), 132, dtype)
+    scale = 1 / math.sqrt(D)
+    ref = oracle.attention_ref(oracle.widen(q, dtype), oracle.widen(k, dtype),
+                               oracle.widen(v, dtype), True, scale)
+    tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
+    outs = []
+    for sched in (None, dict(persistent=0, hkv_major=0, xcd_map=0, queue=0),
+                  dict(persistent=1, hkv_major=0, xcd_map=0, queue=1)):
+        print(f"\n[score jump] k0={k0} schedule={sched}", flush=True)
+        if sched is None:
+            o = bits_of(fa.fwd(tq, tk, tv, causal=True, scale=scale))
+        else:
+            o = bits_of(fa.fwd(tq, tk, tv, causal=True, scale=scale, schedule=sched))
+        parity(oracle.widen(o, dtype), ref, f"k0={k0} schedule={sched}")
+        outs.append(o)
+    assert np.array_equal(outs[1], outs[2])
+
+
 def test_persistent_and_grid_launches_agree_bitwise():
     # the same items computed by the persistent launch, in both orders, with
     # and without the XCD dealing of (batch, kv head) units, and by one
