@@ -157,6 +157,28 @@ def test_varlen_long_sequences_sampled_rows():
         parity(got[q0 + rows, h], ref, f"varlen long b={b} h={h}")
 
 
+@pytest.mark.parametrize("k0", [24.0, 256.0], ids=["rescaled", "overflowed"])
+def test_varlen_score_jump_in_mask_free_tile(k0):
+    # as the dense test of the same name: in sequences 0 and 2 the key at
+    # relative position 700 scores far above the rest for every row and sits
+    # in a mask-free tile of the query blocks from row 1024 on; with k0 = 256
+    # the exp overflows and the item runs again with the max-first softmax
+    dtype, Hq, Hkv, D = "bf16", 4, 2, 128
+    lens = [1536, 300, 1400]
+    cu = offsets(lens)
+    q, k, v = packed_inputs(int(cu[-1]), int(cu[-1]), Hq, Hkv, D, dtype, 771)
+    qf, kf = oracle.widen(q, dtype).astype(np.float32), oracle.widen(k, dtype).astype(np.float32)
+    qf[:, :, 0] = 8.0
+    for b in (0, 2):
+        kf[int(cu[b]) + 700, :, 0] = k0
+    q, k = wl.to_bits(qf, dtype), wl.to_bits(kf, dtype)
+    scale = 1 / math.sqrt(D)
+    got = run_varlen(q, k, v, cu, cu, max(lens), max(lens), True, scale, dtype)
+    ref = oracle.varlen_ref(oracle.widen(q, dtype), oracle.widen(k, dtype),
+                            oracle.widen(v, dtype), cu, cu, True, scale)
+    parity(oracle.widen(got, dtype), ref, f"varlen score jump k0={k0}")
+
+
 def test_varlen_empty_batch_and_empty_queries():
     import torch
     fa = _fa()
