@@ -304,8 +304,9 @@ def test_score_jump_in_mask_free_tile(k0):
     # moves by a power of two); with k0 = 256 the exp overflows and the item
     # is computed again with the max-first softmax.  Every schedule matches
     # the oracle; the grid and the queue-driven persistent launch (whole items
-    # both) give the same bits (the automatic plan here splits items' keys
-    # into parts, whose merge rounds differently).
+    # both) give the same bits (the automatic plan here, and the split launch
+    # with 4-tile parts whose middle parts reach the mask-free steps, cut
+    # items' keys into parts, whose merge rounds differently).
     fa = _fa()
     dtype = "bf16"
     B, Hq, Hkv, S, D = 1, 4, 2, 1536, 128
@@ -322,7 +323,8 @@ def test_score_jump_in_mask_free_tile(k0):
     tq, tk, tv = to_dev(q, dtype), to_dev(k, dtype), to_dev(v, dtype)
     outs = []
     for sched in (None, dict(persistent=0, hkv_major=0, xcd_map=0, queue=0),
-                  dict(persistent=1, hkv_major=0, xcd_map=0, queue=1)):
+                  dict(persistent=1, hkv_major=0, xcd_map=0, queue=1),
+                  dict(persistent=0, hkv_major=0, xcd_map=0, split_tiles=4)):
         print(f"\n[score jump] k0={k0} schedule={sched}", flush=True)
         if sched is None:
             o = bits_of(fa.fwd(tq, tk, tv, causal=True, scale=scale))
