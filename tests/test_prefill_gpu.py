@@ -303,8 +303,8 @@ def test_score_jump_in_mask_free_tile(k0):
     # reference is about 2^19 (above 2^tau but finite: the row's reference
     # moves by a power of two); with k0 = 256 the exp overflows and the item
     # is computed again with the max-first softmax.  Every schedule matches
-    # the oracle; the grid and the queue-driven persistent launch (whole items
-    # both) give the same bits (the automatic plan here, and the split launch
+    # the oracle; the grid, the queue-driven and the snake-order persistent
+    # launches (whole items all) give the same bits (the automatic plan here, and the split launch
     # with 4-tile parts whose middle parts reach the mask-free steps, cut
     # items' keys into parts, whose merge rounds differently).
     fa = _fa()
@@ -324,7 +324,8 @@ def test_score_jump_in_mask_free_tile(k0):
     outs = []
     for sched in (None, dict(persistent=0, hkv_major=0, xcd_map=0, queue=0),
                   dict(persistent=1, hkv_major=0, xcd_map=0, queue=1),
-                  dict(persistent=0, hkv_major=0, xcd_map=0, split_tiles=4)):
+                  dict(persistent=0, hkv_major=0, xcd_map=0, split_tiles=4),
+                  dict(persistent=1, hkv_major=0, xcd_map=0, queue=0)):
         print(f"\n[score jump] k0={k0} schedule={sched}", flush=True)
         if sched is None:
             o = bits_of(fa.fwd(tq, tk, tv, causal=True, scale=scale))
@@ -333,6 +334,7 @@ def test_score_jump_in_mask_free_tile(k0):
         parity(oracle.widen(o, dtype), ref, f"k0={k0} schedule={sched}")
         outs.append(o)
     assert np.array_equal(outs[1], outs[2])
+    assert np.array_equal(outs[1], outs[4])
 
 
 def test_persistent_and_grid_launches_agree_bitwise():
